@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for paged decode attention, cache_write and copy_blocks.
+
+TEST INFRASTRUCTURE ONLY: tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` are the only callers.  The library path
+(``paged_kv_cache_pa_amd``) never imports this package, and this package
+imports nothing from it.
+
+``oracle.c`` (built to ``liboracle.so`` with gcc) holds the arithmetic;
+``brute.py`` holds a pure-Python scalar version for hand-sized inputs.  Each
+function cites the passage of the pages it follows.  Every function here is
+pinned by ``tests/test_oracle.py``; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DT = {"f32": 0, "f16": 1, "bf16": 2}
+_lib = None
+
+
+def build(verbose=False, src=None, out=None) -> str:
+    """Compile oracle.c with gcc (fp64, OpenMP, no fast-math)."""
+    src = src or os.path.join(_HERE, "oracle.c")
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path):
+    """Load a built oracle library and declare its signatures."""
+    L = ctypes.CDLL(path)
+    P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    L.oracle_decode.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, P, I, P, P, I, I]
+    L.oracle_decode_dense.argtypes = [P, P, P, P, D, I, I, I, I, I, I, P, I, P, I]
+    L.oracle_decode_split.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P, I]
+    L.oracle_cache_write.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    L.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, I]
+    L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    L.oracle_half_to_double.restype = D
+    L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    L.oracle_bf16_to_double.restype = D
+    for f in ("oracle_decode", "oracle_decode_dense", "oracle_decode_split",
+              "oracle_cache_write", "oracle_copy_blocks"):
+        getattr(L, f).restype = I
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = load(LIB_PATH)
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype=None):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _threads(n):
+    if n is not None:
+        return int(n)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise OracleError(f"{what} returned {rc}")
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
+           units=None, want_weights=False, nthreads=None):
+    """Paged decode in fp64.  Returns out [S, Hq, D] (float64); with
+    ``want_weights`` also the softmax weights [S, Hq, MBS*B] (zeros past n).
+
+    ``units``: optional int array [(s, h), ...]; only those rows are computed
+    (the rest of ``out`` is zero)."""
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    S, Hq, D = q.shape
+    NB, B, Hkv, _ = k_cache.shape
+    MBS = bt.shape[1]
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    w = np.zeros((S, Hq, MBS * B), dtype=np.float64) if want_weights else None
+    u = None if units is None else _c(units, np.int32).reshape(-1, 2)
+    rc = lib().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                             float(scale), S, Hq, Hkv, D, B, MBS, NB, _DT[dtype],
+                             _ptr(u), 0 if u is None else u.shape[0], _ptr(out), _ptr(w),
+                             MBS * B, _threads(nthreads))
+    _check(rc, "oracle_decode")
+    return (out, w) if want_weights else out
+
+
+def decode_dense(q, k, v, context_lens, scale, dtype, units=None, nthreads=None):
+    """Contiguous-layout decode in fp64; k, v are [S, Smax, Hkv, D]."""
+    q, k, v = _c(q), _c(k), _c(v)
+    cl = _c(context_lens, np.int32)
+    S, Hq, D = q.shape
+    _, Smax, Hkv, _ = k.shape
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    u = None if units is None else _c(units, np.int32).reshape(-1, 2)
+    rc = lib().oracle_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(cl), float(scale),
+                                   S, Hq, Hkv, D, Smax, _DT[dtype], _ptr(u),
+                                   0 if u is None else u.shape[0], _ptr(out),
+                                   _threads(nthreads))
+    _check(rc, "oracle_decode_dense")
+    return out
+
+
+def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
+                 partition_size, nthreads=None):
+    """Paged decode with the context cut into partitions and merged (fp64)."""
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    S, Hq, D = q.shape
+    NB, B, Hkv, _ = k_cache.shape
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    rc = lib().oracle_decode_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                                   float(scale), S, Hq, Hkv, D, B, bt.shape[1], NB, _DT[dtype],
+                                   int(partition_size), _ptr(out), _threads(nthreads))
+    _check(rc, "oracle_decode_split")
+    return out
+
+
+def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, dtype):
+    """Returns new (k_cache, v_cache) copies with the tokens written."""
+    k_new, v_new = _c(k_new), _c(v_new)
+    kc, vc = np.array(k_cache, copy=True, order="C"), np.array(v_cache, copy=True, order="C")
+    sm = _c(slot_mapping, np.int32)
+    NB, B, Hkv, D = kc.shape
+    rc = lib().oracle_cache_write(_ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(vc), _ptr(sm),
+                                  sm.shape[0], NB, B, Hkv, D, _DT[dtype])
+    _check(rc, "oracle_cache_write")
+    return kc, vc
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, dtype):
+    """Returns new (k_cache, v_cache) copies with every (src, dst) block copied."""
+    kc, vc = np.array(k_cache, copy=True, order="C"), np.array(v_cache, copy=True, order="C")
+    bp = _c(block_pairs, np.int32).reshape(-1, 2)
+    NB, B, Hkv, D = kc.shape
+    rc = lib().oracle_copy_blocks(_ptr(kc), _ptr(vc), _ptr(bp), bp.shape[0], NB, B, Hkv, D,
+                                  _DT[dtype])
+    _check(rc, "oracle_copy_blocks")
+    return kc, vc
+
+
+def half_to_double(bits: int) -> float:
+    return lib().oracle_half_to_double(int(bits))
+
+
+def bf16_to_double(bits: int) -> float:
+    return lib().oracle_bf16_to_double(int(bits))
