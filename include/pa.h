@@ -1,0 +1,197 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-KV-cache attention library.
+ *
+ * Pages cited (by title, then section / equation / figure):
+ *   [Kwon] "Efficient Memory Management for Large Language Model Serving
+ *          with PagedAttention" (paper summary page)
+ *   [Int]  "vLLM Internals: PagedAttention, Continuous Batching, and Where
+ *          the 2-4x Comes From"
+ *   [Res]  "Paged Attention: Managing the KV Cache Like Virtual Memory"
+ *   [Os]   the blog.teliaz.com page on PagedAttention as OS paging, section
+ *          "PagedAttention: the OS metaphor, made literal"
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Pointers named as device pointers must point to GPU memory on the
+ *    current HIP device; parameter structs are host memory read during the
+ *    call only.  The caller owns every buffer, including the split-K
+ *    workspace.  The library allocates, frees and synchronises nothing and
+ *    keeps no state between calls (reentrant).
+ *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the legacy default
+ *    stream) and the call returns at once.  Buffers must stay valid until the
+ *    stream has passed the work.
+ *  - Every call returns a pa_status.  All argument checks run on the host
+ *    before any HIP call, so a non-PA_OK status means nothing was enqueued.
+ *    Only PA_ERR_HIP reports a failure of the launch itself.
+ *  - Element types: PA_F32, PA_F16 (IEEE binary16), PA_BF16.  q, the caches,
+ *    the new tokens and out share one dtype.  Indices are int32.
+ *  - Conditions that live in device memory (context lengths, table entries,
+ *    slots, pair ids) cannot be checked on the host.  Out-of-range values
+ *    never cause an out-of-bounds access: each is clamped or skipped as
+ *    stated per entry point, and the result for that sequence / token /
+ *    pair is then unspecified.
+ *
+ * Layouts (row-major, innermost last):
+ *   q, out              [num_seqs, num_q_heads, head_dim]
+ *   k_cache, v_cache    [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables        [num_seqs, max_blocks_per_seq]   int32
+ *   context_lens        [num_seqs]                       int32
+ *   dense k, v          [num_seqs, max_seq_len, num_kv_heads, head_dim]
+ *   k_new, v_new        [num_tokens, num_kv_heads, head_dim]
+ *   slot_mapping        [num_tokens]                     int32
+ *   block_pairs         [num_pairs, 2] (src, dst)        int32
+ * One block of the pool is exactly block_size consecutive token rows of the
+ * dense layout, so paged and dense inputs can hold identical bytes.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL                   */
+    PA_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be,
+                                or inconsistent with another                 */
+    PA_ERR_DTYPE = -3,       /* dtype is not one of pa_dtype                 */
+    PA_ERR_ALIGN = -4,       /* a data pointer is not 16-byte aligned        */
+    PA_ERR_UNSUPPORTED = -5, /* valid but not built: head_dim not 64/128,
+                                query heads per kv head above 8, more than
+                                65535 partitions or 2^31 - 1 (seq, head) rows */
+    PA_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small       */
+    PA_ERR_HIP = -7          /* the HIP launch failed                         */
+} pa_status;
+
+/* Shape of one decode call (host struct). */
+typedef struct {
+    int32_t num_seqs;           /* S >= 0; S == 0 enqueues nothing           */
+    int32_t num_q_heads;        /* Hq >= 1                                    */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 8     */
+    int32_t head_dim;           /* D in {64, 128}                             */
+    int32_t block_size;         /* B, a power of two in [1, 256]; paged only  */
+    int32_t max_blocks_per_seq; /* row stride of block_tables; paged only     */
+    int32_t num_blocks;         /* NB, pool size; paged only                  */
+    int32_t max_context_len;    /* host-known bound on every context_lens[s]; */
+                                /* sizes the split-K grid. Paged: <= MBS * B  */
+    int32_t partition_size;     /* 0: one workgroup covers a whole sequence;  */
+                                /* else split-K over partitions of this many  */
+                                /* tokens, a multiple of B (paged) / of 16    */
+    int32_t dtype;              /* pa_dtype                                   */
+} pa_decode_params;
+
+/* Shape of the pool for cache_write / copy_blocks (host struct). */
+typedef struct {
+    int32_t num_blocks;   /* NB >= 1                                          */
+    int32_t block_size;   /* B, a power of two in [1, 256]                    */
+    int32_t num_kv_heads; /* Hkv >= 1                                         */
+    int32_t head_dim;     /* D >= 1 with D * element bytes a multiple of 16   */
+    int32_t dtype;        /* pa_dtype                                         */
+} pa_cache_params;
+
+/*
+ * Bytes of workspace pa_decode / pa_decode_dense need for ``p``: zero when
+ * partition_size == 0 or max_context_len <= partition_size, otherwise
+ * num_seqs * num_q_heads * ceil(max_context_len / partition_size)
+ * * (head_dim + 2) * 4.  Only the fields the size depends on are checked
+ * (dtype, the head counts, head_dim, num_seqs, max_context_len >= 0,
+ * partition_size >= 0); block_size, max_blocks_per_seq and num_blocks are
+ * not read.  Writes the size to *bytes (0 on error); returns a pa_status.
+ */
+int pa_decode_workspace_size(const pa_decode_params *p, size_t *bytes);
+
+/*
+ * Paged single-query (decode) attention.  For every sequence s and query
+ * head h, with n = context_lens[s] and g = h / (Hq / Hkv):
+ *   out[s][h] = sum_{t<n} a_t v_t,  a_t = exp(x_t) / sum_{u<n} exp(x_u),
+ *   x_t = scale * q[s][h] . k_t,
+ * where token t is read from physical block block_tables[s][t / B], offset
+ * t % B, kv head g of k_cache / v_cache ([Kwon] §3.4 "PagedAttention
+ * Algorithm", the per-token and block-wise equations; block table mapping
+ * in "KV Cache Manager: Block Table Mapping"; [Int] "PagedAttention: page
+ * tables, for KV", address translation).  K and V are gathered straight
+ * through the table with no compaction pass ([Os]).  Query heads sharing a
+ * kv head form contiguous groups ([Res] "Attention over scattered blocks").
+ * Slots at t >= n and table entries at index >= ceil(n / B) are never read.
+ * n == 0 gives a zero row.  Arithmetic is fp32 with the result rounded to
+ * the dtype (round to nearest even).
+ *
+ * q, k_cache, v_cache, block_tables, context_lens, out: device pointers.
+ * workspace: device pointer to at least pa_decode_workspace_size() bytes
+ * when that size is non-zero (may be NULL otherwise); its contents on entry
+ * do not matter and are left unspecified.
+ * Device-side conditions: 0 <= context_lens[s] <= max_context_len and
+ * 0 <= block_tables[s][j] < num_blocks for j < ceil(n / B).  A longer
+ * context is clamped to max_context_len (and to MBS * B); a table entry
+ * outside [0, NB) is clamped into it.
+ * With partition_size > 0 a second kernel (the merge) runs on the same
+ * stream.  Results are bitwise deterministic for fixed inputs and launch
+ * configuration, and independent of where the blocks sit in the pool.
+ */
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale,
+              void *out, const pa_decode_params *p, void *workspace, size_t ws_bytes,
+              void *stream);
+
+/*
+ * The same attention over a contiguous cache: token t of sequence s is row
+ * (s, t) of k, v ([Res] "Attention over scattered blocks": the contiguous
+ * cache addressed directly, no table).  Built from the same kernel source as
+ * pa_decode with only the address function changed, so on identical bytes
+ * the two return bitwise-identical outputs for equal partition_size and
+ * max_context_len (whatever the paged block_size).  block_size, max_blocks_per_seq and
+ * num_blocks in ``p`` are ignored; max_seq_len (>= 1) is the position
+ * stride of k and v and clamps every context length.
+ */
+int pa_decode_dense(const void *q, const void *k, const void *v,
+                    const int32_t *context_lens, float scale, void *out,
+                    const pa_decode_params *p, int32_t max_seq_len,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * cache_write: for every new token i < num_tokens with slot = slot_mapping[i]
+ * in [0, NB * B), copies its K row and V row ([Hkv, D] each, byte for byte)
+ * into block slot / B, offset slot % B of k_cache / v_cache ([Kwon] §3.4
+ * "Kernel-Level Optimizations", item 1, the fused reshape and block write:
+ * one launch, the scheduler names block and slot; [Res] "A paged KV cache,
+ * in code": the slot mapping).  Negative slots are padding and are skipped;
+ * slots >= NB * B are skipped too.  Slots must be distinct within one call
+ * (two tokens for one slot race).
+ * k_new, v_new, slot_mapping, k_cache, v_cache: device pointers.
+ * num_tokens == 0 enqueues nothing.
+ */
+int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *slot_mapping, int32_t num_tokens,
+                   const pa_cache_params *p, void *stream);
+
+/*
+ * copy_blocks: for every pair (src, dst) of block_pairs, copies the whole K
+ * block and the whole V block ([B, Hkv, D] each, byte for byte) from src to
+ * dst, all pairs in one launch ([Kwon] §3.4 "Kernel-Level Optimizations",
+ * item 3, the fused block copy taking (source, destination) pairs; "Memory
+ * Sharing ...": copy-on-write copies the entire block).  Destinations must
+ * be distinct and none may also be a source within one call; pairs with an
+ * id outside [0, NB) are skipped.
+ * k_cache, v_cache, block_pairs: device pointers.  num_pairs == 0 enqueues
+ * nothing.
+ */
+int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs,
+                   int32_t num_pairs, const pa_cache_params *p, void *stream);
+
+/* Static text for a pa_status value (never NULL). */
+const char *pa_status_string(int status);
+
+/* Static text naming the build: target, kernel variants, compiler. */
+const char *pa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,234 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libpa.so`` (C ABI in ``include/pa.h``).  It only
+marshals arguments: shapes are read from the tensors, pointers and the
+current HIP stream are passed through, and every step of the computation
+runs in the library's HIP kernels.  There is no CPU fallback: if the library
+is not built, every call raises.
+
+Entry points (same names as the C ABI):
+  pa_decode, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
+  pa_copy_blocks
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+__all__ = ["pa_decode", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
+           "pa_copy_blocks", "PaError", "lib", "LIB_PATH", "STATUS"]
+
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
+          -4: "PA_ERR_ALIGN", -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_WORKSPACE",
+          -7: "PA_ERR_HIP"}
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = lib().pa_status_string(status).decode()
+        super().__init__(f"{what}: {msg}")
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "max_context_len", "partition_size", "dtype")]
+
+
+class CacheParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_blocks", "block_size", "num_kv_heads", "head_dim", "dtype")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP library {LIB_PATH} is not built; run `python -m paged_kv_cache_pa_amd.build` "
+                "(or __graft_entry__.build()) first. There is no CPU fallback.")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        DP, CP = ctypes.POINTER(DecodeParams), ctypes.POINTER(CacheParams)
+        L.pa_decode_workspace_size.argtypes = [DP, ctypes.POINTER(SZ)]
+        L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
+        L.pa_decode_dense.argtypes = [P, P, P, P, ctypes.c_float, P, DP, I32, P, SZ, P]
+        L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
+        L.pa_copy_blocks.argtypes = [P, P, P, I32, CP, P]
+        for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_dense", "pa_cache_write",
+                  "pa_copy_blocks"):
+            getattr(L, f).restype = ctypes.c_int
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_build_info.argtypes = []
+        L.pa_build_info.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dim=None, dtype=None):
+    import torch
+
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise PaError(rc, what)
+
+
+def _params_paged(q, k_cache, block_tables, max_context_len, partition_size):
+    S, Hq, D = q.shape
+    NB, B, Hkv, _ = k_cache.shape
+    MBS = block_tables.shape[1]
+    return DecodeParams(S, Hq, Hkv, D, B, MBS, NB,
+                        MBS * B if max_context_len is None else int(max_context_len),
+                        int(partition_size), _dtype_code(q))
+
+
+def pa_decode_workspace_size(params: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_decode_workspace_size(ctypes.byref(params), ctypes.byref(n)),
+           "pa_decode_workspace_size")
+    return int(n.value)
+
+
+def _workspace(params, workspace, device):
+    import torch
+
+    need = pa_decode_workspace_size(params)
+    if need and workspace is None:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+              max_context_len=None, partition_size=0, workspace=None, stream=None):
+    """Paged decode attention; writes ``out`` [S, Hq, D] and returns it.
+
+    q [S, Hq, D]; k_cache, v_cache [NB, B, Hkv, D]; block_tables [S, MBS]
+    int32; context_lens [S] int32.  ``max_context_len`` (host-known bound on
+    every context length, default MBS * B) sizes the split-K grid when
+    ``partition_size`` > 0.  A workspace tensor is allocated by torch if one
+    is needed and none is given."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4, q.dtype)
+    _need(v_cache, "v_cache", 4, q.dtype)
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch between k_cache/v_cache or q/out")
+    if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size)
+    ws, nbytes = _workspace(p, workspace, q.device)
+    _check(lib().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                           _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
+                           _ptr(ws), nbytes, _stream(stream)), "pa_decode")
+    return out
+
+
+def pa_decode_dense(q, k, v, context_lens, scale, out, *, max_context_len=None,
+                    partition_size=0, workspace=None, stream=None):
+    """Contiguous-layout twin: k, v [S, max_seq_len, Hkv, D]."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k, "k", 4, q.dtype)
+    _need(v, "v", 4, q.dtype)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v.shape != k.shape or out.shape != q.shape or k.shape[0] != q.shape[0]:
+        raise ValueError("shape mismatch")
+    S, Hq, D = q.shape
+    _, Smax, Hkv, _ = k.shape
+    p = DecodeParams(S, Hq, Hkv, D, 16, 1, 1,
+                     Smax if max_context_len is None else int(max_context_len),
+                     int(partition_size), _dtype_code(q))
+    workspace, nbytes = _workspace(p, workspace, q.device)
+    _check(lib().pa_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(context_lens), float(scale),
+                                 _ptr(out), ctypes.byref(p), int(Smax), _ptr(workspace), nbytes,
+                                 _stream(stream)), "pa_decode_dense")
+    return out
+
+
+def _cache_params(k_cache):
+    NB, B, Hkv, D = k_cache.shape
+    return CacheParams(NB, B, Hkv, D, _dtype_code(k_cache))
+
+
+def pa_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, stream=None):
+    """Scatter new tokens' K/V rows ([N, Hkv, D]) into their slots."""
+    import torch
+
+    _need(k_cache, "k_cache", 4)
+    _need(v_cache, "v_cache", 4, k_cache.dtype)
+    _need(k_new, "k_new", 3, k_cache.dtype)
+    _need(v_new, "v_new", 3, k_cache.dtype)
+    _need(slot_mapping, "slot_mapping", 1, torch.int32)
+    if k_new.shape != v_new.shape or k_new.shape[1:] != k_cache.shape[2:] or \
+            slot_mapping.shape[0] != k_new.shape[0] or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    p = _cache_params(k_cache)
+    _check(lib().pa_cache_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(slot_mapping), int(k_new.shape[0]), ctypes.byref(p),
+                                _stream(stream)), "pa_cache_write")
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
+    """Copy whole K and V blocks for every (src, dst) row of block_pairs [n, 2]."""
+    import torch
+
+    _need(k_cache, "k_cache", 4)
+    _need(v_cache, "v_cache", 4, k_cache.dtype)
+    _need(block_pairs, "block_pairs", 2, torch.int32)
+    if block_pairs.shape[1] != 2 or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    p = _cache_params(k_cache)
+    _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
+                                int(block_pairs.shape[0]), ctypes.byref(p), _stream(stream)),
+           "pa_copy_blocks")

@@ -1,0 +1,195 @@
+// pa_abi.cpp -- the C ABI declared in include/pa.h: host-side argument
+// checks, grid sizing, then one call into the kernel launchers.  No HIP call
+// happens before every check has passed, so every error path is testable
+// without a GPU.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16; }
+
+bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
+    return x >= lo && x <= hi && (x & (x - 1)) == 0;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by the paged and dense decode.  ``row_limit`` is the most
+// tokens a sequence can hold (MBS * B paged, max_seq_len dense); ``granule``
+// is what partition_size must be a multiple of.
+int check_decode_shape(const pa_decode_params *p, int64_t row_limit, int32_t granule) {
+    if (!p) return PA_ERR_NULL;
+    if (!dtype_ok(p->dtype)) return PA_ERR_DTYPE;
+    if (p->num_seqs < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
+        return PA_ERR_SHAPE;
+    if (p->num_q_heads % p->num_kv_heads) return PA_ERR_SHAPE;
+    if (p->max_context_len < 0 || p->max_context_len > row_limit) return PA_ERR_SHAPE;
+    if (p->partition_size < 0 || (p->partition_size && p->partition_size % granule))
+        return PA_ERR_SHAPE;
+    if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (p->num_q_heads / p->num_kv_heads > 8) return PA_ERR_UNSUPPORTED;
+    // Grid x is num_seqs * num_kv_heads (the merge uses num_seqs * num_q_heads)
+    // and must fit 31 bits; grid y is the partition count.
+    if ((int64_t)p->num_seqs * p->num_q_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+    if (p->partition_size &&
+        ((int64_t)p->max_context_len + p->partition_size - 1) / p->partition_size > 65535)
+        return PA_ERR_UNSUPPORTED;
+    return PA_OK;
+}
+
+int check_paged_shape(const pa_decode_params *p) {
+    if (!p) return PA_ERR_NULL;
+    if (!pow2_in(p->block_size, 1, 256)) return PA_ERR_SHAPE;
+    if (p->max_blocks_per_seq < 1 || p->num_blocks < 1) return PA_ERR_SHAPE;
+    return check_decode_shape(p, (int64_t)p->max_blocks_per_seq * p->block_size, p->block_size);
+}
+
+int32_t num_partitions(const pa_decode_params *p) {
+    if (p->partition_size == 0 || p->max_context_len <= p->partition_size) return 1;
+    return (p->max_context_len + p->partition_size - 1) / p->partition_size;
+}
+
+size_t workspace_bytes(const pa_decode_params *p) {
+    const int32_t P = num_partitions(p);
+    if (P <= 1) return 0;
+    return (size_t)p->num_seqs * p->num_q_heads * P * (p->head_dim + 2) * sizeof(float);
+}
+
+int run_decode(const void *q, const void *k, const void *v, const int32_t *tables,
+               const int32_t *lens, float scale, void *out, const pa_decode_params *p,
+               void *ws, size_t ws_bytes, void *stream, bool dense, int32_t max_seq_len) {
+    if (p->num_seqs == 0) return PA_OK;
+    if (!q || !k || !v || !lens || !out || (!dense && !tables)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGN;
+    if (((uintptr_t)lens & 3u) || (tables && ((uintptr_t)tables & 3u))) return PA_ERR_ALIGN;
+    const size_t need = workspace_bytes(p);
+    if (need) {
+        if (!ws || ws_bytes < need) return PA_ERR_WORKSPACE;
+        if ((uintptr_t)ws & 3u) return PA_ERR_ALIGN;
+    }
+    pa::DecodeLaunch l;
+    l.q = q;
+    l.k = k;
+    l.v = v;
+    l.tables = tables;
+    l.lens = lens;
+    l.out = out;
+    l.ws = (float *)ws;
+    l.scale = scale;
+    l.S = p->num_seqs;
+    l.Hq = p->num_q_heads;
+    l.Hkv = p->num_kv_heads;
+    l.D = p->head_dim;
+    l.dtype = p->dtype;
+    l.B = dense ? 0 : p->block_size;
+    l.MBS = dense ? 0 : p->max_blocks_per_seq;
+    l.NB = dense ? 0 : p->num_blocks;
+    l.max_ctx = p->max_context_len;
+    l.P = num_partitions(p);
+    l.PS = l.P > 1 ? p->partition_size : 0;
+    l.pos_stride = dense ? max_seq_len : 0;
+    l.dense = dense;
+    const int e = pa::launch_decode(l, stream);
+    return e ? PA_ERR_HIP : PA_OK;
+}
+
+int check_cache_params(const pa_cache_params *p) {
+    if (!p) return PA_ERR_NULL;
+    if (!dtype_ok(p->dtype)) return PA_ERR_DTYPE;
+    if (p->num_blocks < 1 || p->num_kv_heads < 1 || p->head_dim < 1) return PA_ERR_SHAPE;
+    if (!pow2_in(p->block_size, 1, 256)) return PA_ERR_SHAPE;
+    if (((int64_t)p->head_dim * elem_bytes(p->dtype)) % 16) return PA_ERR_SHAPE;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_workspace_size(const pa_decode_params *p, size_t *bytes) {
+    if (!bytes || !p) return PA_ERR_NULL;
+    *bytes = 0;
+    // The size depends on S, Hq, D, max_context_len and partition_size only,
+    // so the same call serves pa_decode and pa_decode_dense.
+    const int st = check_decode_shape(p, INT32_MAX, 1);
+    if (st != PA_OK) return st;
+    *bytes = workspace_bytes(p);
+    return PA_OK;
+}
+
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, const int32_t *context_lens, float scale, void *out,
+              const pa_decode_params *p, void *workspace, size_t ws_bytes, void *stream) {
+    const int st = check_paged_shape(p);
+    if (st != PA_OK) return st;
+    return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
+                      ws_bytes, stream, false, 0);
+}
+
+int pa_decode_dense(const void *q, const void *k, const void *v, const int32_t *context_lens,
+                    float scale, void *out, const pa_decode_params *p, int32_t max_seq_len,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    if (!p) return PA_ERR_NULL;
+    if (max_seq_len < 1) return PA_ERR_SHAPE;
+    const int st = check_decode_shape(p, max_seq_len, 16);
+    if (st != PA_OK) return st;
+    return run_decode(q, k, v, nullptr, context_lens, scale, out, p, workspace, ws_bytes, stream,
+                      true, max_seq_len);
+}
+
+int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                   const int32_t *slot_mapping, int32_t num_tokens, const pa_cache_params *p,
+                   void *stream) {
+    const int st = check_cache_params(p);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        ((uintptr_t)slot_mapping & 3u))
+        return PA_ERR_ALIGN;
+    const int64_t row = (int64_t)p->num_kv_heads * p->head_dim * elem_bytes(p->dtype);
+    const int e = pa::launch_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
+                                         (int64_t)p->num_blocks * p->block_size, row, stream);
+    return e ? PA_ERR_HIP : PA_OK;
+}
+
+int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int32_t num_pairs,
+                   const pa_cache_params *p, void *stream) {
+    const int st = check_cache_params(p);
+    if (st != PA_OK) return st;
+    if (num_pairs < 0) return PA_ERR_SHAPE;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_pairs & 3u))
+        return PA_ERR_ALIGN;
+    const int64_t blk = (int64_t)p->block_size * p->num_kv_heads * p->head_dim *
+                        elem_bytes(p->dtype);
+    const int e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, p->num_blocks,
+                                         blk, stream);
+    return e ? PA_ERR_HIP : PA_OK;
+}
+
+const char *pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK: success";
+        case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+        case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size is out of range or inconsistent";
+        case PA_ERR_DTYPE: return "PA_ERR_DTYPE: unknown element type";
+        case PA_ERR_ALIGN: return "PA_ERR_ALIGN: a data pointer is not aligned";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim or head grouping not built";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-K workspace missing or too small";
+        case PA_ERR_HIP: return "PA_ERR_HIP: the HIP launch failed";
+    }
+    return "unknown pa_status";
+}
+
+const char *pa_build_info(void) { return pa::kernel_build_info(); }
+
+}  // extern "C"

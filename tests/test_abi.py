@@ -1,0 +1,205 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point
+``include/pa.h`` declares, and rejects bad arguments before any HIP call.
+No kernel is launched here (every call below fails validation or has
+nothing to do)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_pa_amd as pa
+from paged_kv_cache_pa_amd import CacheParams, DecodeParams
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(pa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return pa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"pa_decode", "pa_decode_dense", "pa_cache_write", "pa_copy_blocks",
+            "pa_decode_workspace_size", "pa_status_string", "pa_build_info"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/ but not exported"
+
+
+def test_status_strings(L):
+    for code, name in pa.STATUS.items():
+        assert L.pa_status_string(code).decode().startswith(name)
+    assert L.pa_status_string(12345)
+    assert b"gfx950" in L.pa_build_info()
+
+
+def params(**kw):
+    base = dict(num_seqs=4, num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+                max_blocks_per_seq=7, num_blocks=64, max_context_len=112, partition_size=0,
+                dtype=0)
+    base.update(kw)
+    return DecodeParams(*[base[f] for f, _ in DecodeParams._fields_])
+
+
+class Buf:
+    """Aligned host memory standing in for device pointers (never dereferenced:
+    every call using it fails validation first)."""
+
+    def __init__(self, n=4096):
+        self.raw = ctypes.create_string_buffer(n + 64)
+        base = ctypes.addressof(self.raw)
+        self.p = ctypes.c_void_p((base + 15) & ~15)
+        self.odd = ctypes.c_void_p(((base + 15) & ~15) + 2)
+
+
+def decode(L, p, q=None, k=None, v=None, t=None, c=None, out=None, ws=None, nbytes=0):
+    b = Buf()
+    args = [b.p if x is None else x for x in (q, k, v, t, c)]
+    return L.pa_decode(*args, ctypes.c_float(0.125), b.p if out is None else out,
+                       ctypes.byref(p), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(num_seqs=-1), SHAPE), (dict(num_q_heads=0), SHAPE), (dict(num_kv_heads=0), SHAPE),
+    (dict(num_q_heads=12, num_kv_heads=5), SHAPE), (dict(block_size=12), SHAPE),
+    (dict(block_size=512), SHAPE), (dict(block_size=0), SHAPE),
+    (dict(max_blocks_per_seq=0), SHAPE), (dict(num_blocks=0), SHAPE),
+    (dict(max_context_len=-1), SHAPE), (dict(max_context_len=7 * 16 + 1), SHAPE),
+    (dict(partition_size=8), SHAPE), (dict(partition_size=-16), SHAPE),
+    (dict(head_dim=96), UNSUP), (dict(head_dim=256), UNSUP),
+    (dict(num_q_heads=18, num_kv_heads=2), UNSUP),
+])
+def test_decode_rejects_bad_shapes(L, kw, code):
+    assert decode(L, params(**kw)) == code
+
+
+def test_decode_rejects_null_and_misaligned(L):
+    b = Buf()
+    p = params()
+    for i in range(6):
+        args = [b.p] * 6
+        args[i] = None
+        assert L.pa_decode(*args[:5], ctypes.c_float(1.0), args[5], ctypes.byref(p), None, 0,
+                           None) == NULL
+    for i in (0, 1, 2, 5):  # q, k, v, out must be 16-byte aligned
+        args = [b.p] * 6
+        args[i] = b.odd
+        assert L.pa_decode(*args[:5], ctypes.c_float(1.0), args[5], ctypes.byref(p), None, 0,
+                           None) == ALIGN
+    assert L.pa_decode(b.p, b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p, None, None, 0,
+                       None) == NULL
+
+
+def test_decode_split_needs_workspace(L):
+    p = params(partition_size=32)
+    need = pa.pa_decode_workspace_size(p)
+    assert need == 4 * 8 * 4 * (64 + 2) * 4  # ceil(112 / 32) = 4 partitions
+    b = Buf(need + 64)
+    assert decode(L, p) == WS
+    assert decode(L, p, ws=b.p, nbytes=need - 4) == WS
+
+
+def test_workspace_size_formula():
+    assert pa.pa_decode_workspace_size(params()) == 0
+    assert pa.pa_decode_workspace_size(params(partition_size=112)) == 0   # one partition
+    assert pa.pa_decode_workspace_size(params(partition_size=16)) == 4 * 8 * 7 * 66 * 4
+    big = params(num_seqs=8, num_q_heads=12, num_kv_heads=2, head_dim=128, max_blocks_per_seq=1024,
+                 max_context_len=16384, partition_size=512, dtype=2)
+    assert pa.pa_decode_workspace_size(big) == 8 * 12 * 32 * 130 * 4
+    with pytest.raises(pa.PaError):
+        pa.pa_decode_workspace_size(params(dtype=9))
+
+
+def test_zero_sequences_is_a_no_op(L):
+    p = params(num_seqs=0)
+    assert L.pa_decode(None, None, None, None, None, ctypes.c_float(1.0), None, ctypes.byref(p),
+                       None, 0, None) == OK
+
+
+def test_dense_checks(L):
+    b = Buf()
+    p = params(max_context_len=100)
+    assert L.pa_decode_dense(b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p, ctypes.byref(p), 0,
+                             None, 0, None) == SHAPE               # max_seq_len < 1
+    assert L.pa_decode_dense(b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p, ctypes.byref(p), 64,
+                             None, 0, None) == SHAPE               # max_context_len > max_seq_len
+    p = params(max_context_len=100, partition_size=24)
+    assert L.pa_decode_dense(b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p, ctypes.byref(p), 128,
+                             None, 0, None) == SHAPE               # partition not a multiple of 16
+    p = params(max_context_len=100, partition_size=32)
+    assert L.pa_decode_dense(b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p, ctypes.byref(p), 128,
+                             None, 0, None) == WS
+    p = params(num_seqs=0, max_context_len=1)
+    assert L.pa_decode_dense(None, None, None, None, ctypes.c_float(1.0), None, ctypes.byref(p), 1,
+                             None, 0, None) == OK
+
+
+def cparams(**kw):
+    base = dict(num_blocks=64, block_size=16, num_kv_heads=8, head_dim=64, dtype=0)
+    base.update(kw)
+    return CacheParams(*[base[f] for f, _ in CacheParams._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), DTYPE), (dict(num_blocks=0), SHAPE), (dict(block_size=3), SHAPE),
+    (dict(num_kv_heads=0), SHAPE), (dict(head_dim=0), SHAPE),
+    (dict(head_dim=6, dtype=1), SHAPE),   # 12-byte rows cannot be moved as 16-byte vectors
+])
+def test_cache_write_and_copy_reject_bad_params(L, kw, code):
+    b = Buf()
+    p = cparams(**kw)
+    assert L.pa_cache_write(b.p, b.p, b.p, b.p, b.p, 4, ctypes.byref(p), None) == code
+    assert L.pa_copy_blocks(b.p, b.p, b.p, 4, ctypes.byref(p), None) == code
+
+
+def test_cache_write_and_copy_pointer_checks(L):
+    b = Buf()
+    p = cparams()
+    assert L.pa_cache_write(b.p, b.p, b.p, b.p, b.p, -1, ctypes.byref(p), None) == SHAPE
+    assert L.pa_cache_write(None, None, None, None, None, 0, ctypes.byref(p), None) == OK
+    for i in range(5):
+        args = [b.p] * 5
+        args[i] = None
+        assert L.pa_cache_write(*args, 3, ctypes.byref(p), None) == NULL
+    for i in range(4):
+        args = [b.p] * 5
+        args[i] = b.odd
+        assert L.pa_cache_write(*args, 3, ctypes.byref(p), None) == ALIGN
+    assert L.pa_copy_blocks(b.p, b.p, b.p, -2, ctypes.byref(p), None) == SHAPE
+    assert L.pa_copy_blocks(None, None, None, 0, ctypes.byref(p), None) == OK
+    assert L.pa_copy_blocks(b.p, None, b.p, 2, ctypes.byref(p), None) == NULL
+    assert L.pa_copy_blocks(b.odd, b.p, b.p, 2, ctypes.byref(p), None) == ALIGN
+    assert L.pa_cache_write(b.p, b.p, b.p, b.p, b.p, 3, None, None) == NULL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 64)
+    with pytest.raises(ValueError):
+        pa.pa_decode(q, q, q, q, q, 1.0, q)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+
+    monkeypatch.setattr(pa, "_lib", None)
+    monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        pa.lib()
+    importlib.reload(pa)

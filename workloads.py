@@ -421,3 +421,32 @@ def random_with_dense(seed, dtype, lens, hq, hkv, d, block_size=16, smax=None,
     q = randn(rng, (S, hq, d), dtype)
     return Paged(dtype, q, k, v, table, lens, 1.0 / math.sqrt(d), B, 0,
                  k_dense=kd, v_dense=vd, name=f"ragged-dense-{dtype}-s{seed}")
+
+
+def config3_device(batch, ctx, seed=303, device="cuda"):
+    """Config 3 point generated on the device (torch's Philox generator), for
+    sizes whose host generation would take minutes.  Same structure as
+    ``config3``: dense [S, n, 40, 128] fp16 values, cut into 16-token blocks,
+    block i stored at pool id pi(i) (numpy PCG64 permutation).  Returns a dict
+    of device tensors."""
+    import torch
+
+    H, D, B = 40, 128, 16
+    assert ctx % B == 0
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1000003 + batch * 7919 + ctx)
+    shape = (batch, ctx, H, D)
+    k_dense = torch.randn(shape, generator=g, device=device, dtype=torch.float32).half()
+    v_dense = torch.randn(shape, generator=g, device=device, dtype=torch.float32).half()
+    q = torch.randn((batch, H, D), generator=g, device=device, dtype=torch.float32).half()
+    NB = batch * ctx // B
+    perm = np.random.default_rng(seed + 7919 * batch + ctx).permutation(NB).astype(np.int64)
+    pt = torch.from_numpy(perm).to(device)
+    k = torch.empty((NB, B, H, D), dtype=torch.float16, device=device)
+    v = torch.empty_like(k)
+    k[pt] = k_dense.view(NB, B, H, D)
+    v[pt] = v_dense.view(NB, B, H, D)
+    table = pt.to(torch.int32).view(batch, ctx // B).contiguous()
+    lens = torch.full((batch,), ctx, dtype=torch.int32, device=device)
+    return dict(q=q, k_cache=k, v_cache=v, block_tables=table, context_lens=lens,
+                k_dense=k_dense, v_dense=v_dense, scale=1.0 / math.sqrt(D))
