@@ -69,7 +69,9 @@ def time_events(fn, iters, stream):
 
 
 def paged_dense_ratio(points, iters=20, warm=5):
-    """Config 3: paged vs dense decode on identical bytes, interleaved."""
+    """Config 3: paged vs dense decode on identical values, interleaved round
+    by round, in both layouts (token-major: the pool is the dense buffer cut
+    into blocks; head-major: both transposed to [.., Hkv, tokens, D])."""
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -80,26 +82,32 @@ def paged_dense_ratio(points, iters=20, warm=5):
     for batch, ctx in points:
         d = W.config3_device(batch, ctx)
         out = torch.empty_like(d["q"])
-        args_p = (d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["context_lens"],
-                  d["scale"], out)
+        for layout in ("NHD", "HND"):
+            if layout == "HND":  # same values, head-major
+                for key in ("k_cache", "v_cache", "k_dense", "v_dense"):
+                    d[key] = d[key].transpose(1, 2).contiguous()
 
-        def paged(i):
-            pa.pa_decode(*args_p, max_context_len=ctx)
+            def paged(i):
+                pa.pa_decode(d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                             d["context_lens"], d["scale"], out, max_context_len=ctx,
+                             layout=layout)
 
-        def dense(i):
-            pa.pa_decode_dense(d["q"], d["k_dense"], d["v_dense"], d["context_lens"], d["scale"],
-                               out, max_context_len=ctx)
+            def dense(i):
+                pa.pa_decode_dense(d["q"], d["k_dense"], d["v_dense"], d["context_lens"],
+                                   d["scale"], out, max_context_len=ctx, layout=layout)
 
-        for _ in range(warm):
-            paged(0)
-            dense(0)
-        tp, td = [], []
-        for _ in range(iters):  # interleave round by round
-            tp += time_events(paged, 1, st)
-            td += time_events(dense, 1, st)
-        mp, md = float(np.median(tp)), float(np.median(td))
-        res[f"{batch}x{ctx}"] = {"paged_us": round(mp * 1e6, 2), "dense_us": round(md * 1e6, 2),
-                                 "ratio": round(mp / md, 4)}
+            for _ in range(warm):
+                paged(0)
+                dense(0)
+            tp, td = [], []
+            for _ in range(iters):
+                tp += time_events(paged, 1, st)
+                td += time_events(dense, 1, st)
+            mp, md = float(np.median(tp)), float(np.median(td))
+            nbytes = batch * ctx * 40 * 128 * 2 * 2
+            res[f"{layout} {batch}x{ctx}"] = {
+                "paged_us": round(mp * 1e6, 2), "dense_us": round(md * 1e6, 2),
+                "ratio": round(mp / md, 4), "paged_GB_s": round(nbytes / mp / 1e9, 1)}
         del d, out
         torch.cuda.empty_cache()
     return res
@@ -177,6 +185,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0,
                     help="split-K partition size for pa_decode (0 = none)")
     ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--layout", choices=("NHD", "HND"), default="HND",
+                    help="KV pool layout: token-major or head-major blocks")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the dense ratio, copy_blocks and CPU legs (for profiling runs)")
     args = ap.parse_args()
@@ -209,14 +219,19 @@ def main():
     q = torch.from_numpy(p.q).to(dev)
     bt = torch.from_numpy(p.block_tables).to(dev)
     cl = torch.from_numpy(lens).to(dev)
-    kc0 = torch.from_numpy(p.k_cache).to(dev)
-    vc0 = torch.from_numpy(p.v_cache).to(dev)
+    if args.layout == "HND":  # same values, head-major blocks [NB, Hkv, B, D]
+        kc0 = torch.from_numpy(np.ascontiguousarray(np.swapaxes(p.k_cache, 1, 2))).to(dev)
+        vc0 = torch.from_numpy(np.ascontiguousarray(np.swapaxes(p.v_cache, 1, 2))).to(dev)
+    else:
+        kc0 = torch.from_numpy(p.k_cache).to(dev)
+        vc0 = torch.from_numpy(p.v_cache).to(dev)
     R = max(1, args.replicas)
     pools = [(kc0, vc0)] + [(kc0.clone(), vc0.clone()) for _ in range(R - 1)]
     out = torch.empty_like(q)
     mcl = int(lens.max())
     ws_bytes = pa.pa_decode_workspace_size(pa.DecodeParams(S, Hq, Hkv, D, B, p.max_blocks_per_seq,
-                                                           NB, mcl, args.partition, 1))
+                                                           NB, mcl, args.partition, 1,
+                                                           pa.LAYOUTS[args.layout]))
     ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -224,11 +239,11 @@ def main():
 
     def step(i, timed=False):
         k, v = pools[i % R]
-        pa.pa_cache_write(k_new, v_new, k, v, slots)
+        pa.pa_cache_write(k_new, v_new, k, v, slots, layout=args.layout)
         if timed:
             ev[i][0].record(stream)
         pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl,
-                     partition_size=args.partition, workspace=ws)
+                     partition_size=args.partition, workspace=ws, layout=args.layout)
         if timed:
             ev[i][1].record(stream)
 
@@ -270,11 +285,12 @@ def main():
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "sum_context_lens": toks, "max_context_len": mcl,
             "num_blocks": NB, "partition_size": args.partition, "kv_pool_replicas": R,
+            "kv_layout": "[NB, Hkv, B, D]" if args.layout == "HND" else "[NB, B, Hkv, D]",
             "seed": 202,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<_Float16,128,1,false>" + (" + merge_kernel" if args.partition else ""),
+            "kernel": "decode_kernel<_Float16,128,1,kPagedWide>" + (" + merge_kernel" if args.partition else ""),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -286,7 +302,7 @@ def main():
     }
     if not args.no_extras:
         try:
-            result["paged_vs_dense"] = paged_dense_ratio([(8, 2048), (32, 1024), (128, 2048)])
+            result["paged_vs_dense"] = paged_dense_ratio([(8, 256), (32, 1024), (128, 2048)])
         except Exception as e:  # report, do not hide the main result
             result["paged_vs_dense"] = {"error": repr(e)}
         log("paged/dense done")

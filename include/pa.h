@@ -33,15 +33,20 @@
  *
  * Layouts (row-major, innermost last):
  *   q, out              [num_seqs, num_q_heads, head_dim]
- *   k_cache, v_cache    [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_cache, v_cache    token-major: [num_blocks, block_size, num_kv_heads, head_dim]
+ *                       head-major:  [num_blocks, num_kv_heads, block_size, head_dim]
  *   block_tables        [num_seqs, max_blocks_per_seq]   int32
  *   context_lens        [num_seqs]                       int32
- *   dense k, v          [num_seqs, max_seq_len, num_kv_heads, head_dim]
+ *   dense k, v          token-major: [num_seqs, max_seq_len, num_kv_heads, head_dim]
+ *                       head-major:  [num_seqs, num_kv_heads, max_seq_len, head_dim]
  *   k_new, v_new        [num_tokens, num_kv_heads, head_dim]
  *   slot_mapping        [num_tokens]                     int32
  *   block_pairs         [num_pairs, 2] (src, dst)        int32
- * One block of the pool is exactly block_size consecutive token rows of the
- * dense layout, so paged and dense inputs can hold identical bytes.
+ * In the token-major layout one block is exactly block_size consecutive
+ * token rows of the token-major dense layout, so paged and dense inputs can
+ * hold identical bytes.  The head-major layout keeps each (block, kv head)
+ * contiguous ([Res] "A paged KV cache, in code": a pool of [blocks, kv
+ * heads, 16 tokens, head dimension]); the decode kernel streams it faster.
  */
 #ifndef PA_H
 #define PA_H
@@ -55,6 +60,9 @@ extern "C" {
 
 typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
 
+/* Order of the dimensions inside a block (paged) or a sequence (dense). */
+typedef enum { PA_LAYOUT_TOKEN_MAJOR = 0, PA_LAYOUT_HEAD_MAJOR = 1 } pa_kv_layout;
+
 typedef enum {
     PA_OK = 0,
     PA_ERR_NULL = -1,        /* a required pointer is NULL                   */
@@ -64,7 +72,8 @@ typedef enum {
     PA_ERR_ALIGN = -4,       /* a data pointer is not 16-byte aligned        */
     PA_ERR_UNSUPPORTED = -5, /* valid but not built: head_dim not 64/128,
                                 query heads per kv head above 8, more than
-                                65535 partitions or 2^31 - 1 (seq, head) rows */
+                                65535 partitions or 2^31 - 1 (seq, head) rows,
+                                a token row (all kv heads) above 128 MiB      */
     PA_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small       */
     PA_ERR_HIP = -7          /* the HIP launch failed                         */
 } pa_status;
@@ -84,6 +93,7 @@ typedef struct {
                                 /* else split-K over partitions of this many  */
                                 /* tokens, a multiple of B (paged) / of 16    */
     int32_t dtype;              /* pa_dtype                                   */
+    int32_t layout;             /* pa_kv_layout of the K and V buffers        */
 } pa_decode_params;
 
 /* Shape of the pool for cache_write / copy_blocks (host struct). */
@@ -93,6 +103,7 @@ typedef struct {
     int32_t num_kv_heads; /* Hkv >= 1                                         */
     int32_t head_dim;     /* D >= 1 with D * element bytes a multiple of 16   */
     int32_t dtype;        /* pa_dtype                                         */
+    int32_t layout;       /* pa_kv_layout of the pool                         */
 } pa_cache_params;
 
 /*
@@ -112,7 +123,7 @@ int pa_decode_workspace_size(const pa_decode_params *p, size_t *bytes);
  *   out[s][h] = sum_{t<n} a_t v_t,  a_t = exp(x_t) / sum_{u<n} exp(x_u),
  *   x_t = scale * q[s][h] . k_t,
  * where token t is read from physical block block_tables[s][t / B], offset
- * t % B, kv head g of k_cache / v_cache ([Kwon] §3.4 "PagedAttention
+ * t % B, kv head g of k_cache / v_cache in p->layout ([Kwon] §3.4 "PagedAttention
  * Algorithm", the per-token and block-wise equations; block table mapping
  * in "KV Cache Manager: Block Table Mapping"; [Int] "PagedAttention: page
  * tables, for KV", address translation).  K and V are gathered straight
@@ -162,7 +173,8 @@ int pa_decode_dense(const void *q, const void *k, const void *v,
  * one launch, the scheduler names block and slot; [Res] "A paged KV cache,
  * in code": the slot mapping).  Negative slots are padding and are skipped;
  * slots >= NB * B are skipped too.  Slots must be distinct within one call
- * (two tokens for one slot race).
+ * (two tokens for one slot race).  In the head-major layout each kv head's
+ * row lands in its own (block, head) plane.
  * k_new, v_new, slot_mapping, k_cache, v_cache: device pointers.
  * num_tokens == 0 enqueues nothing.
  */

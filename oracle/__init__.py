@@ -21,6 +21,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _DT = {"f32": 0, "f16": 1, "bf16": 2}
+_LAYOUT = {"NHD": 0, "HND": 1}  # token-major [.., tokens, Hkv, D] / head-major [.., Hkv, tokens, D]
+
+
+def _dims(a, layout):
+    """(outer, tokens, kv heads, head_dim) of a pool or dense tensor."""
+    x, y, z, d = a.shape
+    return (x, y, z, d) if _LAYOUT[layout] == 0 else (x, z, y, d)
 _lib = None
 
 
@@ -42,10 +49,10 @@ def load(path):
     """Load a built oracle library and declare its signatures."""
     L = ctypes.CDLL(path)
     P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-    L.oracle_decode.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, P, I, P, P, I, I]
-    L.oracle_decode_dense.argtypes = [P, P, P, P, D, I, I, I, I, I, I, P, I, P, I]
-    L.oracle_decode_split.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P, I]
-    L.oracle_cache_write.argtypes = [P, P, P, P, P, I, I, I, I, I, I]
+    L.oracle_decode.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, P, I, P, P, I, I]
+    L.oracle_decode_dense.argtypes = [P, P, P, P, D, I, I, I, I, I, I, I, P, I, P, I]
+    L.oracle_decode_split.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, I, P, I]
+    L.oracle_cache_write.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I]
     L.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, I]
     L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     L.oracle_half_to_double.restype = D
@@ -93,7 +100,7 @@ def _check(rc, what):
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
-           units=None, want_weights=False, nthreads=None):
+           units=None, want_weights=False, nthreads=None, layout="NHD"):
     """Paged decode in fp64.  Returns out [S, Hq, D] (float64); with
     ``want_weights`` also the softmax weights [S, Hq, MBS*B] (zeros past n).
 
@@ -102,29 +109,30 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
     S, Hq, D = q.shape
-    NB, B, Hkv, _ = k_cache.shape
+    NB, B, Hkv, _ = _dims(k_cache, layout)
     MBS = bt.shape[1]
     out = np.zeros((S, Hq, D), dtype=np.float64)
     w = np.zeros((S, Hq, MBS * B), dtype=np.float64) if want_weights else None
     u = None if units is None else _c(units, np.int32).reshape(-1, 2)
     rc = lib().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
                              float(scale), S, Hq, Hkv, D, B, MBS, NB, _DT[dtype],
-                             _ptr(u), 0 if u is None else u.shape[0], _ptr(out), _ptr(w),
+                             _LAYOUT[layout], _ptr(u), 0 if u is None else u.shape[0], _ptr(out), _ptr(w),
                              MBS * B, _threads(nthreads))
     _check(rc, "oracle_decode")
     return (out, w) if want_weights else out
 
 
-def decode_dense(q, k, v, context_lens, scale, dtype, units=None, nthreads=None):
-    """Contiguous-layout decode in fp64; k, v are [S, Smax, Hkv, D]."""
+def decode_dense(q, k, v, context_lens, scale, dtype, units=None, nthreads=None, layout="NHD"):
+    """Contiguous-layout decode in fp64; k, v are [S, Smax, Hkv, D] ("NHD")
+    or [S, Hkv, Smax, D] ("HND")."""
     q, k, v = _c(q), _c(k), _c(v)
     cl = _c(context_lens, np.int32)
     S, Hq, D = q.shape
-    _, Smax, Hkv, _ = k.shape
+    _, Smax, Hkv, _ = _dims(k, layout)
     out = np.zeros((S, Hq, D), dtype=np.float64)
     u = None if units is None else _c(units, np.int32).reshape(-1, 2)
     rc = lib().oracle_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(cl), float(scale),
-                                   S, Hq, Hkv, D, Smax, _DT[dtype], _ptr(u),
+                                   S, Hq, Hkv, D, Smax, _DT[dtype], _LAYOUT[layout], _ptr(u),
                                    0 if u is None else u.shape[0], _ptr(out),
                                    _threads(nthreads))
     _check(rc, "oracle_decode_dense")
@@ -132,37 +140,38 @@ def decode_dense(q, k, v, context_lens, scale, dtype, units=None, nthreads=None)
 
 
 def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
-                 partition_size, nthreads=None):
+                 partition_size, nthreads=None, layout="NHD"):
     """Paged decode with the context cut into partitions and merged (fp64)."""
     q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
     bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
     S, Hq, D = q.shape
-    NB, B, Hkv, _ = k_cache.shape
+    NB, B, Hkv, _ = _dims(k_cache, layout)
     out = np.zeros((S, Hq, D), dtype=np.float64)
     rc = lib().oracle_decode_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
                                    float(scale), S, Hq, Hkv, D, B, bt.shape[1], NB, _DT[dtype],
-                                   int(partition_size), _ptr(out), _threads(nthreads))
+                                   _LAYOUT[layout], int(partition_size), _ptr(out), _threads(nthreads))
     _check(rc, "oracle_decode_split")
     return out
 
 
-def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, dtype):
+def cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, dtype, layout="NHD"):
     """Returns new (k_cache, v_cache) copies with the tokens written."""
     k_new, v_new = _c(k_new), _c(v_new)
     kc, vc = np.array(k_cache, copy=True, order="C"), np.array(v_cache, copy=True, order="C")
     sm = _c(slot_mapping, np.int32)
-    NB, B, Hkv, D = kc.shape
+    NB, B, Hkv, D = _dims(kc, layout)
     rc = lib().oracle_cache_write(_ptr(k_new), _ptr(v_new), _ptr(kc), _ptr(vc), _ptr(sm),
-                                  sm.shape[0], NB, B, Hkv, D, _DT[dtype])
+                                  sm.shape[0], NB, B, Hkv, D, _DT[dtype], _LAYOUT[layout])
     _check(rc, "oracle_cache_write")
     return kc, vc
 
 
-def copy_blocks(k_cache, v_cache, block_pairs, dtype):
-    """Returns new (k_cache, v_cache) copies with every (src, dst) block copied."""
+def copy_blocks(k_cache, v_cache, block_pairs, dtype, layout="NHD"):
+    """Returns new (k_cache, v_cache) copies with every (src, dst) block copied
+    (a block is one contiguous range in either layout)."""
     kc, vc = np.array(k_cache, copy=True, order="C"), np.array(v_cache, copy=True, order="C")
     bp = _c(block_pairs, np.int32).reshape(-1, 2)
-    NB, B, Hkv, D = kc.shape
+    NB, B, Hkv, D = _dims(kc, layout)
     rc = lib().oracle_copy_blocks(_ptr(kc), _ptr(vc), _ptr(bp), bp.shape[0], NB, B, Hkv, D,
                                   _DT[dtype])
     _check(rc, "oracle_copy_blocks")

@@ -22,6 +22,11 @@
  * Storage dtypes: 0 = fp32, 1 = fp16 (IEEE binary16), 2 = bf16.  Every
  * element is widened to double exactly before any arithmetic.
  *
+ * Layouts: 0 = token-major blocks [NB, B, Hkv, D] (dense [S, Smax, Hkv, D]);
+ * 1 = head-major blocks [NB, Hkv, B, D] (dense [S, Hkv, Smax, D]), the
+ * [blocks, kv heads, 16 tokens, head dim] pool of [Res] "A paged KV cache,
+ * in code".
+ *
  * Return codes: 0 ok, -1 bad argument, -2 an index (block id, slot, table
  * entry) outside its range.  Nothing is written before the arguments are
  * checked.
@@ -105,11 +110,6 @@ static void attend(const double *qv, const double *K, const double *V, int n, in
     }
 }
 
-/* One unit of work: (sequence s, query head h). */
-typedef struct {
-    int S, Hq, Hkv, D;
-} shape_t;
-
 static int check_shape(int S, int Hq, int Hkv, int D, int dtype) {
     if (S < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return -1;
     if (Hq % Hkv) return -1;
@@ -117,21 +117,26 @@ static int check_shape(int S, int Hq, int Hkv, int D, int dtype) {
     return 0;
 }
 
+/* Element index of (block b, offset o, kv head g, dim 0) in a pool. */
+static size_t pool_index(int layout, size_t b, size_t o, size_t g, int B, int Hkv, int D) {
+    if (layout == 0) return ((b * B + o) * Hkv + g) * D;
+    return ((b * Hkv + g) * B + o) * D;
+}
+
 /*
  * Gather: sequence s's token t lives at physical block
  * block_tables[s][t / B], offset t % B ([Int] "PagedAttention: page tables,
  * for KV", the resolve() address translation; [Kwon] §3.4 "KV Cache Manager:
- * Block Table Mapping").  Pool layout [NB, B, Hkv, D].  Query head h reads
- * kv head h / G, G = Hq / Hkv: contiguous groups of query heads share one kv
- * head ([Res] "Attention over scattered blocks": the 6 query heads sharing
- * one key/value row).
+ * Block Table Mapping").  Query head h reads kv head h / G, G = Hq / Hkv:
+ * contiguous groups of query heads share one kv head ([Res] "Attention over
+ * scattered blocks": the 6 query heads sharing one key/value row).
  */
 static int gather_seq(const void *cache, const int32_t *row, int n, int B, int NB,
-                      int Hkv, int D, int g, int dtype, double *dst) {
+                      int Hkv, int D, int g, int dtype, int layout, double *dst) {
     for (int t = 0; t < n; ++t) {
         int32_t b = row[t / B];
         if (b < 0 || b >= NB) return -2;
-        size_t base = (((size_t)b * B + (size_t)(t % B)) * Hkv + g) * D;
+        size_t base = pool_index(layout, (size_t)b, (size_t)(t % B), (size_t)g, B, Hkv, D);
         for (int d = 0; d < D; ++d) dst[(size_t)t * D + d] = load(cache, base + d, dtype);
     }
     return 0;
@@ -144,10 +149,11 @@ static int gather_seq(const void *cache, const int32_t *row, int n, int B, int N
  */
 int oracle_decode(const void *q, const void *k_cache, const void *v_cache,
                   const int32_t *block_tables, const int32_t *context_lens, double scale,
-                  int S, int Hq, int Hkv, int D, int B, int MBS, int NB, int dtype,
+                  int S, int Hq, int Hkv, int D, int B, int MBS, int NB, int dtype, int layout,
                   const int32_t *units, int n_units, double *out, double *weights,
                   int wstride, int nthreads) {
     if (check_shape(S, Hq, Hkv, D, dtype) || B <= 0 || MBS <= 0 || NB <= 0) return -1;
+    if (layout != 0 && layout != 1) return -1;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return -1;
     for (int s = 0; s < S; ++s) {
         int n = context_lens[s];
@@ -182,8 +188,8 @@ int oracle_decode(const void *q, const void *k_cache, const void *v_cache,
             err = -1;
         } else {
             const int32_t *row = block_tables + (size_t)s * MBS;
-            int e1 = gather_seq(k_cache, row, n, B, NB, Hkv, D, g, dtype, K);
-            int e2 = gather_seq(v_cache, row, n, B, NB, Hkv, D, g, dtype, V);
+            int e1 = gather_seq(k_cache, row, n, B, NB, Hkv, D, g, dtype, layout, K);
+            int e2 = gather_seq(v_cache, row, n, B, NB, Hkv, D, g, dtype, layout, V);
             if (e1 || e2) {
                 err = -2;
             } else {
@@ -198,15 +204,17 @@ int oracle_decode(const void *q, const void *k_cache, const void *v_cache,
 }
 
 /*
- * Dense (contiguous) decode: k, v are [S, Smax, Hkv, D]; token t of sequence
- * s is row (s, t).  Same attention as above, no table ([Res] "Attention over
- * scattered blocks": the contiguous cache addressed directly).
+ * Dense (contiguous) decode: k, v are [S, Smax, Hkv, D] (layout 0) or
+ * [S, Hkv, Smax, D] (layout 1); token t of sequence s is row (s, t).  Same
+ * attention as above, no table ([Res] "Attention over scattered blocks":
+ * the contiguous cache addressed directly).
  */
 int oracle_decode_dense(const void *q, const void *k, const void *v,
                         const int32_t *context_lens, double scale, int S, int Hq, int Hkv,
-                        int D, int Smax, int dtype, const int32_t *units, int n_units,
-                        double *out, int nthreads) {
+                        int D, int Smax, int dtype, int layout, const int32_t *units,
+                        int n_units, double *out, int nthreads) {
     if (check_shape(S, Hq, Hkv, D, dtype) || Smax <= 0) return -1;
+    if (layout != 0 && layout != 1) return -1;
     if (!q || !k || !v || !context_lens || !out) return -1;
     for (int s = 0; s < S; ++s)
         if (context_lens[s] < 0 || context_lens[s] > Smax) return -2;
@@ -234,7 +242,8 @@ int oracle_decode_dense(const void *q, const void *k, const void *v,
             err = -1;
         } else {
             for (int t = 0; t < n; ++t) {
-                size_t base = (((size_t)s * Smax + t) * Hkv + g) * D;
+                size_t base = layout == 0 ? (((size_t)s * Smax + t) * Hkv + g) * D
+                                          : (((size_t)s * Hkv + g) * Smax + t) * D;
                 for (int d = 0; d < D; ++d) {
                     K[(size_t)t * D + d] = load(k, base + d, dtype);
                     V[(size_t)t * D + d] = load(v, base + d, dtype);
@@ -262,8 +271,9 @@ int oracle_decode_dense(const void *q, const void *k, const void *v,
 int oracle_decode_split(const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *block_tables, const int32_t *context_lens,
                         double scale, int S, int Hq, int Hkv, int D, int B, int MBS, int NB,
-                        int dtype, int P, double *out, int nthreads) {
+                        int dtype, int layout, int P, double *out, int nthreads) {
     if (check_shape(S, Hq, Hkv, D, dtype) || B <= 0 || MBS <= 0 || NB <= 0 || P <= 0) return -1;
+    if (layout != 0 && layout != 1) return -1;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return -1;
     for (int s = 0; s < S; ++s)
         if (context_lens[s] < 0 || context_lens[s] > MBS * B) return -2;
@@ -288,8 +298,8 @@ int oracle_decode_split(const void *q, const void *k_cache, const void *v_cache,
             goto done;
         }
         const int32_t *row = block_tables + (size_t)s * MBS;
-        if (gather_seq(k_cache, row, n, B, NB, Hkv, D, g, dtype, K) ||
-            gather_seq(v_cache, row, n, B, NB, Hkv, D, g, dtype, V)) {
+        if (gather_seq(k_cache, row, n, B, NB, Hkv, D, g, dtype, layout, K) ||
+            gather_seq(v_cache, row, n, B, NB, Hkv, D, g, dtype, layout, V)) {
             err = -2;
             goto done;
         }
@@ -335,21 +345,27 @@ int oracle_decode_split(const void *q, const void *k_cache, const void *v_cache,
  * 1: the write goes to the physical block and slot the scheduler names;
  * [Res] "A paged KV cache, in code": the slot mapping).  A negative slot is
  * padding and is skipped.  Slots >= NB * B are an error (nothing written).
+ * Each kv head's [D] row is placed at (block, offset, head) of the layout.
  */
 int oracle_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                        const int32_t *slot_mapping, int N, int NB, int B, int Hkv, int D,
-                       int dtype) {
+                       int dtype, int layout) {
     if (N < 0 || NB <= 0 || B <= 0 || Hkv <= 0 || D <= 0 || dtype < 0 || dtype > 2) return -1;
+    if (layout != 0 && layout != 1) return -1;
     if (N > 0 && (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)) return -1;
     for (int i = 0; i < N; ++i)
         if (slot_mapping[i] >= (int64_t)NB * B) return -2;
-    size_t row = (size_t)Hkv * D * elem_bytes(dtype);
+    size_t e = elem_bytes(dtype), row = (size_t)D * e;
     for (int i = 0; i < N; ++i) {
         int32_t slot = slot_mapping[i];
         if (slot < 0) continue;
-        size_t dst = ((size_t)(slot / B) * B + (size_t)(slot % B)) * row;
-        memcpy((char *)k_cache + dst, (const char *)k_new + (size_t)i * row, row);
-        memcpy((char *)v_cache + dst, (const char *)v_new + (size_t)i * row, row);
+        for (int g = 0; g < Hkv; ++g) {
+            size_t dst = pool_index(layout, (size_t)(slot / B), (size_t)(slot % B), (size_t)g,
+                                    B, Hkv, D) * e;
+            size_t src = ((size_t)i * Hkv + g) * row;
+            memcpy((char *)k_cache + dst, (const char *)k_new + src, row);
+            memcpy((char *)v_cache + dst, (const char *)v_new + src, row);
+        }
     }
     return 0;
 }

@@ -35,12 +35,27 @@ class PaError(RuntimeError):
 class DecodeParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
-        "max_blocks_per_seq", "num_blocks", "max_context_len", "partition_size", "dtype")]
+        "max_blocks_per_seq", "num_blocks", "max_context_len", "partition_size", "dtype",
+        "layout")]
 
 
 class CacheParams(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "num_blocks", "block_size", "num_kv_heads", "head_dim", "dtype")]
+        "num_blocks", "block_size", "num_kv_heads", "head_dim", "dtype", "layout")]
+
+LAYOUTS = {"NHD": 0, "HND": 1}  # token-major [.., tokens, Hkv, D] / head-major [.., Hkv, tokens, D]
+
+
+def _layout(layout) -> int:
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {list(LAYOUTS)}, got {layout!r}")
+    return LAYOUTS[layout]
+
+
+def pool_dims(k_cache, layout="NHD"):
+    """(num_blocks, block_size, num_kv_heads, head_dim) of a pool tensor."""
+    NB, a, b, D = k_cache.shape
+    return (NB, a, b, D) if _layout(layout) == 0 else (NB, b, a, D)
 
 
 _lib = None
@@ -117,13 +132,13 @@ def _check(rc, what):
         raise PaError(rc, what)
 
 
-def _params_paged(q, k_cache, block_tables, max_context_len, partition_size):
+def _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout):
     S, Hq, D = q.shape
-    NB, B, Hkv, _ = k_cache.shape
+    NB, B, Hkv, _ = pool_dims(k_cache, layout)
     MBS = block_tables.shape[1]
     return DecodeParams(S, Hq, Hkv, D, B, MBS, NB,
                         MBS * B if max_context_len is None else int(max_context_len),
-                        int(partition_size), _dtype_code(q))
+                        int(partition_size), _dtype_code(q), _layout(layout))
 
 
 def pa_decode_workspace_size(params: DecodeParams) -> int:
@@ -144,11 +159,13 @@ def _workspace(params, workspace, device):
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
-              max_context_len=None, partition_size=0, workspace=None, stream=None):
+              max_context_len=None, partition_size=0, workspace=None, stream=None,
+              layout="NHD"):
     """Paged decode attention; writes ``out`` [S, Hq, D] and returns it.
 
-    q [S, Hq, D]; k_cache, v_cache [NB, B, Hkv, D]; block_tables [S, MBS]
-    int32; context_lens [S] int32.  ``max_context_len`` (host-known bound on
+    q [S, Hq, D]; k_cache, v_cache [NB, B, Hkv, D] (layout "NHD") or
+    [NB, Hkv, B, D] ("HND"); block_tables [S, MBS] int32; context_lens [S]
+    int32.  ``max_context_len`` (host-known bound on
     every context length, default MBS * B) sizes the split-K grid when
     ``partition_size`` > 0.  A workspace tensor is allocated by torch if one
     is needed and none is given."""
@@ -164,7 +181,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
         raise ValueError("shape mismatch between k_cache/v_cache or q/out")
     if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
         raise ValueError("block_tables / context_lens must have one row per sequence")
-    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size)
+    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout)
     ws, nbytes = _workspace(p, workspace, q.device)
     _check(lib().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
@@ -173,8 +190,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
 
 
 def pa_decode_dense(q, k, v, context_lens, scale, out, *, max_context_len=None,
-                    partition_size=0, workspace=None, stream=None):
-    """Contiguous-layout twin: k, v [S, max_seq_len, Hkv, D]."""
+                    partition_size=0, workspace=None, stream=None, layout="NHD"):
+    """Contiguous-layout twin: k, v [S, max_seq_len, Hkv, D] ("NHD") or
+    [S, Hkv, max_seq_len, D] ("HND")."""
     import torch
 
     _need(q, "q", 3)
@@ -185,10 +203,10 @@ def pa_decode_dense(q, k, v, context_lens, scale, out, *, max_context_len=None,
     if v.shape != k.shape or out.shape != q.shape or k.shape[0] != q.shape[0]:
         raise ValueError("shape mismatch")
     S, Hq, D = q.shape
-    _, Smax, Hkv, _ = k.shape
+    _, Smax, Hkv, _ = pool_dims(k, layout)
     p = DecodeParams(S, Hq, Hkv, D, 16, 1, 1,
                      Smax if max_context_len is None else int(max_context_len),
-                     int(partition_size), _dtype_code(q))
+                     int(partition_size), _dtype_code(q), _layout(layout))
     workspace, nbytes = _workspace(p, workspace, q.device)
     _check(lib().pa_decode_dense(_ptr(q), _ptr(k), _ptr(v), _ptr(context_lens), float(scale),
                                  _ptr(out), ctypes.byref(p), int(Smax), _ptr(workspace), nbytes,
@@ -196,12 +214,12 @@ def pa_decode_dense(q, k, v, context_lens, scale, out, *, max_context_len=None,
     return out
 
 
-def _cache_params(k_cache):
-    NB, B, Hkv, D = k_cache.shape
-    return CacheParams(NB, B, Hkv, D, _dtype_code(k_cache))
+def _cache_params(k_cache, layout):
+    NB, B, Hkv, D = pool_dims(k_cache, layout)
+    return CacheParams(NB, B, Hkv, D, _dtype_code(k_cache), _layout(layout))
 
 
-def pa_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, stream=None):
+def pa_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, stream=None, layout="NHD"):
     """Scatter new tokens' K/V rows ([N, Hkv, D]) into their slots."""
     import torch
 
@@ -210,16 +228,16 @@ def pa_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, *, stream=None)
     _need(k_new, "k_new", 3, k_cache.dtype)
     _need(v_new, "v_new", 3, k_cache.dtype)
     _need(slot_mapping, "slot_mapping", 1, torch.int32)
-    if k_new.shape != v_new.shape or k_new.shape[1:] != k_cache.shape[2:] or \
+    p = _cache_params(k_cache, layout)
+    if k_new.shape != v_new.shape or tuple(k_new.shape[1:]) != (p.num_kv_heads, p.head_dim) or \
             slot_mapping.shape[0] != k_new.shape[0] or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch")
-    p = _cache_params(k_cache)
     _check(lib().pa_cache_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(slot_mapping), int(k_new.shape[0]), ctypes.byref(p),
                                 _stream(stream)), "pa_cache_write")
 
 
-def pa_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
+def pa_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None, layout="NHD"):
     """Copy whole K and V blocks for every (src, dst) row of block_pairs [n, 2]."""
     import torch
 
@@ -228,7 +246,7 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None):
     _need(block_pairs, "block_pairs", 2, torch.int32)
     if block_pairs.shape[1] != 2 or v_cache.shape != k_cache.shape:
         raise ValueError("shape mismatch")
-    p = _cache_params(k_cache)
+    p = _cache_params(k_cache, layout)
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
                                 int(block_pairs.shape[0]), ctypes.byref(p), _stream(stream)),
            "pa_copy_blocks")

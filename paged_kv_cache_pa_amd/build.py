@@ -26,7 +26,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            # packed fp32 VALU ops stay off (no v_pk_*_f32 anywhere in this library)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-command-line-argument",

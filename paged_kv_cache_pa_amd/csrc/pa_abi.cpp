@@ -20,6 +20,10 @@ bool pow2_in(int32_t x, int32_t lo, int32_t hi) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool layout_ok(int32_t layout) {
+    return layout == PA_LAYOUT_TOKEN_MAJOR || layout == PA_LAYOUT_HEAD_MAJOR;
+}
+
 // Checks shared by the paged and dense decode.  ``row_limit`` is the most
 // tokens a sequence can hold (MBS * B paged, max_seq_len dense); ``granule``
 // is what partition_size must be a multiple of.
@@ -29,11 +33,15 @@ int check_decode_shape(const pa_decode_params *p, int64_t row_limit, int32_t gra
     if (p->num_seqs < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1)
         return PA_ERR_SHAPE;
     if (p->num_q_heads % p->num_kv_heads) return PA_ERR_SHAPE;
+    if (!layout_ok(p->layout)) return PA_ERR_SHAPE;
     if (p->max_context_len < 0 || p->max_context_len > row_limit) return PA_ERR_SHAPE;
     if (p->partition_size < 0 || (p->partition_size && p->partition_size % granule))
         return PA_ERR_SHAPE;
     if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
     if (p->num_q_heads / p->num_kv_heads > 8) return PA_ERR_UNSUPPORTED;
+    // In-step row offsets are 32-bit: 16 token rows must span under 4 GiB.
+    if ((int64_t)p->num_kv_heads * p->head_dim * elem_bytes(p->dtype) > (1 << 27))
+        return PA_ERR_UNSUPPORTED;
     // Grid x is num_seqs * num_kv_heads (the merge uses num_seqs * num_q_heads)
     // and must fit 31 bits; grid y is the partition count.
     if ((int64_t)p->num_seqs * p->num_q_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
@@ -94,6 +102,7 @@ int run_decode(const void *q, const void *k, const void *v, const int32_t *table
     l.P = num_partitions(p);
     l.PS = l.P > 1 ? p->partition_size : 0;
     l.pos_stride = dense ? max_seq_len : 0;
+    l.layout = p->layout;
     l.dense = dense;
     const int e = pa::launch_decode(l, stream);
     return e ? PA_ERR_HIP : PA_OK;
@@ -105,6 +114,7 @@ int check_cache_params(const pa_cache_params *p) {
     if (p->num_blocks < 1 || p->num_kv_heads < 1 || p->head_dim < 1) return PA_ERR_SHAPE;
     if (!pow2_in(p->block_size, 1, 256)) return PA_ERR_SHAPE;
     if (((int64_t)p->head_dim * elem_bytes(p->dtype)) % 16) return PA_ERR_SHAPE;
+    if (!layout_ok(p->layout)) return PA_ERR_SHAPE;
     return PA_OK;
 }
 
@@ -154,9 +164,10 @@ int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
         ((uintptr_t)slot_mapping & 3u))
         return PA_ERR_ALIGN;
-    const int64_t row = (int64_t)p->num_kv_heads * p->head_dim * elem_bytes(p->dtype);
+    const int64_t row = (int64_t)p->head_dim * elem_bytes(p->dtype);  // one head's row
     const int e = pa::launch_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
-                                         (int64_t)p->num_blocks * p->block_size, row, stream);
+                                         p->num_blocks, p->block_size, p->num_kv_heads, row,
+                                         p->layout, stream);
     return e ? PA_ERR_HIP : PA_OK;
 }
 

@@ -15,10 +15,15 @@
 //    so one wave load instruction covers R = 64/LPR whole rows and every
 //    byte fetched is used.  A wave step is 16 consecutive tokens (U = 16/R
 //    loads of K and U of V); the four waves take steps round robin and
-//    prefetch their next step's K and V before computing the current one.
+//    issue their next step's loads before computing the current one.  K and
+//    V are streamed once, so they are read with non-temporal loads.
+//  * Two pool layouts are addressed through strides: token-major blocks
+//    [NB, B, Hkv, D] and head-major blocks [NB, Hkv, B, D] ([Res] "A paged
+//    KV cache, in code" keeps [blocks, kv heads, 16 tokens, head dim]).  In
+//    the head-major layout a 16-token step of one head is 4 KiB contiguous.
 //  * The sequence's block-table slice is staged in LDS (up to 1024 entries
 //    at a time), so address translation ([Int] "PagedAttention: page
-//    tables, for KV") costs an LDS read, not a dependent HBM read.
+//    tables, for KV") costs an LDS read per step, not a dependent HBM read.
 //  * q.k: per-lane partial dot (v_dot2_f32_f16 / v_dot2_f32_bf16 on the
 //    unscaled inputs, fp32 FMA for fp32), then a DPP butterfly inside each
 //    LPR-lane row group; every lane of the group ends with the same bits.
@@ -32,6 +37,11 @@
 //    arithmetic.  The reduction order depends only on logical token order,
 //    never on where blocks sit, so paged and dense results are bitwise equal
 //    and invariant to block placement.
+//  * Scheduling: for batches of up to 256 sequences every workgroup ranks the
+//    sequences by context length (longest first, ties by index) and takes
+//    the sequence whose rank matches its grid position, so the longest
+//    sequences start first and the tail of the launch is short.  Which
+//    workgroup computes a row never changes its arithmetic.
 //  * Split-K: partition p covers tokens [p*PS, (p+1)*PS) and writes its
 //    unnormalised partial (acc, m, l) to the workspace; a merge kernel then
 //    combines the partitions by the log-sum-exp identity ([Int] "The kernel
@@ -46,11 +56,13 @@ namespace pa {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+typedef uint32_t vec4 __attribute__((ext_vector_type(4)));  // 16 bytes
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kStepTokens = 16;     // tokens per wave step
 constexpr int kTableChunk = 1024;   // block-table entries staged in LDS at once
+constexpr int kRankMaxSeqs = 256;   // longest-first scheduling up to this batch
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.402823466e38f;  // running-max start (finite)
 
@@ -77,6 +89,14 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ vec4 load_stream(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const vec4 *>(p));
+}
+
+__device__ __forceinline__ vec4 load_cached(const char *p) {
+    return *reinterpret_cast<const vec4 *>(p);
+}
+
 // ---------------------------------------------------------------- element traits
 
 template <typename T>
@@ -85,14 +105,14 @@ struct Elem;
 template <>
 struct Elem<float> {
     static constexpr int kEPL = 4;  // elements per 16 bytes
-    __device__ static float dot(const uint4 &a, const uint4 &b) {
+    __device__ static float dot(const vec4 &a, const vec4 &b) {
         float s = __uint_as_float(a.x) * __uint_as_float(b.x);
         s = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), s);
         s = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), s);
         s = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), s);
         return s;
     }
-    __device__ static void widen(const uint4 &v, float *f) {
+    __device__ static void widen(const vec4 &v, float *f) {
         f[0] = __uint_as_float(v.x);
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
@@ -101,23 +121,29 @@ struct Elem<float> {
     __device__ static void store(void *out, int64_t i, float x) { ((float *)out)[i] = x; }
 };
 
+// Reinterpret one 32-bit lane value as two 16-bit elements.  The value is
+// taken by copy: bit-casting an ext_vector element in place (v.y, v.z, ...)
+// reads element 0 with this compiler.
+__device__ __forceinline__ half2_t as_half2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+__device__ __forceinline__ bf162_t as_bf162(uint32_t w) { return __builtin_bit_cast(bf162_t, w); }
+
 template <>
 struct Elem<_Float16> {
     static constexpr int kEPL = 8;
-    __device__ static float dot(const uint4 &a, const uint4 &b) {
+    __device__ static float dot(const vec4 &a, const vec4 &b) {
         // fp16 x fp16 products are exact in fp32; the sum accumulates in fp32.
-        float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.x), __builtin_bit_cast(half2_t, b.x), 0.0f, false);
-        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.y), __builtin_bit_cast(half2_t, b.y), s, false);
-        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.z), __builtin_bit_cast(half2_t, b.z), s, false);
-        s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a.w), __builtin_bit_cast(half2_t, b.w), s, false);
+        float s = __builtin_amdgcn_fdot2(as_half2(a.x), as_half2(b.x), 0.0f, false);
+        s = __builtin_amdgcn_fdot2(as_half2(a.y), as_half2(b.y), s, false);
+        s = __builtin_amdgcn_fdot2(as_half2(a.z), as_half2(b.z), s, false);
+        s = __builtin_amdgcn_fdot2(as_half2(a.w), as_half2(b.w), s, false);
         return s;
     }
     __device__ static void widen1(uint32_t w, float *f) {
-        half2_t h = __builtin_bit_cast(half2_t, w);
+        const half2_t h = as_half2(w);
         f[0] = (float)h.x;
         f[1] = (float)h.y;
     }
-    __device__ static void widen(const uint4 &v, float *f) {
+    __device__ static void widen(const vec4 &v, float *f) {
         widen1(v.x, f);
         widen1(v.y, f + 2);
         widen1(v.z, f + 4);
@@ -129,19 +155,19 @@ struct Elem<_Float16> {
 template <>
 struct Elem<__bf16> {
     static constexpr int kEPL = 8;
-    __device__ static float dot(const uint4 &a, const uint4 &b) {
+    __device__ static float dot(const vec4 &a, const vec4 &b) {
         // bf16 x bf16 products are exact in fp32; the sum accumulates in fp32.
-        float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a.x), __builtin_bit_cast(bf162_t, b.x), 0.0f, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a.y), __builtin_bit_cast(bf162_t, b.y), s, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a.z), __builtin_bit_cast(bf162_t, b.z), s, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a.w), __builtin_bit_cast(bf162_t, b.w), s, false);
+        float s = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a.x), as_bf162(b.x), 0.0f, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a.y), as_bf162(b.y), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a.z), as_bf162(b.z), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(as_bf162(a.w), as_bf162(b.w), s, false);
         return s;
     }
     __device__ static void widen1(uint32_t w, float *f) {
         f[0] = __uint_as_float(w << 16);          // bf16 is the top half of an fp32
         f[1] = __uint_as_float(w & 0xFFFF0000u);
     }
-    __device__ static void widen(const uint4 &v, float *f) {
+    __device__ static void widen(const vec4 &v, float *f) {
         widen1(v.x, f);
         widen1(v.y, f + 2);
         widen1(v.z, f + 4);
@@ -162,12 +188,22 @@ struct DecodeArgs {
     float *ws_acc;   // [S, Hq, P, D]
     float *ws_ml;    // [S, Hq, P, 2]
     float qk_scale;  // scale * log2(e)
-    int32_t Hq, Hkv, NB, MBS, log2B, max_ctx, PS, P;
-    int64_t row_bytes;   // bytes between consecutive token rows: Hkv * D * e
-    int64_t pos_stride;  // dense: rows per sequence (max_seq_len)
+    int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, PS, P;
+    int32_t rank;       // 1: longest-first sequence order (S <= kRankMaxSeqs)
+    int64_t tok_bytes;  // bytes between consecutive tokens of one head
+    int64_t head_bytes; // bytes between kv heads at a fixed token
+    int64_t blk_bytes;  // paged: bytes per block
+    int64_t seq_bytes;  // dense: bytes per sequence
 };
 
-template <typename T, int D, int G, bool DENSE>
+// Address modes of the decode kernel.
+enum : int {
+    kDense = 0,      // contiguous cache, one base per sequence
+    kPagedWide = 1,  // paged, B >= 16: every 16-token step lies inside one block
+    kPagedNarrow = 2 // paged, B < 16: a step spans several blocks
+};
+
+template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     using E = Elem<T>;
     constexpr int EPL = E::kEPL;
@@ -180,19 +216,45 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     static_assert(U * R == kStepTokens, "step shape");
 
     __shared__ float smem[SMEM];
+    __shared__ int32_t s_len[kRankMaxSeqs];
+    __shared__ int32_t s_pick;
     int32_t *s_tab = reinterpret_cast<int32_t *>(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int rg = lane / LPR;   // row group
     const int c = lane % LPR;    // 16-byte chunk of the row
     const int h = blockIdx.x % a.Hkv;
-    const int s = blockIdx.x / a.Hkv;
     const int part = blockIdx.y;
 
-    int n = a.lens[s];
-    n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    int s, n;
+    if (a.rank) {
+        // Longest-first: rank(t) = #{u : n_u > n_t} + #{u < t : n_u == n_t};
+        // this workgroup serves the sequence of rank blockIdx.x / Hkv.
+        for (int t = tid; t < a.S; t += kThreads) {
+            const int x = a.lens[t];
+            s_len[t] = x < 0 ? 0 : (x > a.max_ctx ? a.max_ctx : x);
+        }
+        __syncthreads();
+        const int want = blockIdx.x / a.Hkv;
+        for (int t = tid; t < a.S; t += kThreads) {
+            const int nt = s_len[t];
+            int r = 0;
+            for (int u = 0; u < a.S; ++u) {
+                const int nu = s_len[u];
+                r += (nu > nt) | ((nu == nt) & (u < t));
+            }
+            if (r == want) s_pick = t;
+        }
+        __syncthreads();
+        s = s_pick;
+        n = s_len[s];
+    } else {
+        s = blockIdx.x / a.Hkv;
+        n = a.lens[s];
+        n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+    }
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;  // first query head of the group
@@ -205,10 +267,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
 
     // q for the G heads of the group: this lane's 16-byte chunk, unscaled.
-    uint4 qv[G];
+    vec4 qv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g)
-        qv[g] = *reinterpret_cast<const uint4 *>(a.q + ((qrow0 + g) * D + (int64_t)c * EPL) * sizeof(T));
+        qv[g] = load_cached(a.q + ((qrow0 + g) * D + (int64_t)c * EPL) * sizeof(T));
 
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -219,22 +281,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         for (int e = 0; e < EPL; ++e) acc[g][e] = 0.0f;
     }
 
-    // Byte offset of this lane's chunk inside a token row of kv head h.
-    const int64_t lane_off = ((int64_t)h * D + (int64_t)c * EPL) * sizeof(T);
-    const char *kbase = a.k + lane_off;
-    const char *vbase = a.v + lane_off;
+    // Per-lane byte offset of its 16-byte chunk of token u*R + rg of a step.
+    const uint32_t tok_bytes = (uint32_t)a.tok_bytes;
+    const uint32_t chunk_off = (uint32_t)(c * EPL * (int)sizeof(T));
+    uint32_t voff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) voff[u] = (uint32_t)(u * R + rg) * tok_bytes + chunk_off;
     const int B = 1 << a.log2B;
-    const int32_t *trow = DENSE ? nullptr : a.tables + (int64_t)s * a.MBS;
-    const int64_t seq_row0 = DENSE ? (int64_t)s * a.pos_stride : 0;
+    const int32_t *trow = MODE == kDense ? nullptr : a.tables + (int64_t)s * a.MBS;
+    // Base of kv head h (and, dense, of sequence s).
+    const int64_t head0 = (int64_t)h * a.head_bytes + (MODE == kDense ? (int64_t)s * a.seq_bytes : 0);
+    const char *kh = a.k + head0;
+    const char *vh = a.v + head0;
 
     const int nblk = (te - tb + B - 1) >> a.log2B;
-    const int chunk_blocks = DENSE ? nblk : kTableChunk;
+    const int chunk_blocks = MODE == kDense ? nblk : kTableChunk;
 
     for (int cb = 0; cb < nblk; cb += chunk_blocks) {
         const int cn = min(chunk_blocks, nblk - cb);
         const int ctb = tb + cb * B;                 // first token of this chunk
         const int cte = min(te, ctb + cn * B);       // one past its last token
-        if constexpr (!DENSE) {
+        if constexpr (MODE != kDense) {
             __syncthreads();  // the previous chunk's readers are done
             const int b0 = (tb >> a.log2B) + cb;
             for (int i = tid; i < cn; i += kThreads) {
@@ -243,33 +310,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             }
             __syncthreads();
         }
-        const int nsteps = (cte - ctb + kStepTokens - 1) / kStepTokens;
+        const int nfull = (cte - ctb) / kStepTokens;      // steps with 16 valid tokens
+        const int tail = (cte - ctb) % kStepTokens;        // valid tokens of the last step
 
-        // Row address of this lane's token for load u of step j.
-        auto row_ptr = [&](const char *base, int j, int u) -> const char * {
-            int t = ctb + j * kStepTokens + u * R + rg;
-            t = t < cte ? t : cte - 1;  // masked rows re-read the last valid token
-            int64_t row;
-            if constexpr (DENSE) {
-                row = seq_row0 + t;
-            } else {
-                int rel = t - ctb;
-                row = (int64_t)s_tab[rel >> a.log2B] * B + (t & (B - 1));
-            }
-            return base + row * a.row_bytes;
-        };
-        auto load = [&](uint4 (&kb)[U], uint4 (&vb)[U], int j) {
+        // Issue the K and V loads of step j (tokens ctb + 16 j ...).  With
+        // MASKED, rows past the end re-read the last valid token.
+        auto issue = [&]<bool MASKED>(vec4 (&kb)[U], vec4 (&vb)[U], int j) {
+            const int t0 = ctb + j * kStepTokens;
+            if constexpr (MODE == kPagedNarrow) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                kb[u] = *reinterpret_cast<const uint4 *>(row_ptr(kbase, j, u));
-                vb[u] = *reinterpret_cast<const uint4 *>(row_ptr(vbase, j, u));
+                for (int u = 0; u < U; ++u) {
+                    int t = t0 + u * R + rg;
+                    if (MASKED) t = t < cte ? t : cte - 1;
+                    const int64_t off = (int64_t)s_tab[(t - ctb) >> a.log2B] * a.blk_bytes +
+                                        (int64_t)(t & (B - 1)) * a.tok_bytes + chunk_off;
+                    kb[u] = load_stream(kh + off);
+                    vb[u] = load_stream(vh + off);
+                }
+            } else {
+                int64_t base;
+                if constexpr (MODE == kDense) {
+                    base = (int64_t)t0 * a.tok_bytes;
+                } else {
+                    const int phys = __builtin_amdgcn_readfirstlane(s_tab[(t0 - ctb) >> a.log2B]);
+                    base = (int64_t)phys * a.blk_bytes + (int64_t)(t0 & (B - 1)) * a.tok_bytes;
+                }
+                const char *kp = kh + base;
+                const char *vp = vh + base;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    uint32_t o = voff[u];
+                    if (MASKED) {
+                        const int r = min(u * R + rg, cte - 1 - t0);
+                        o = (uint32_t)r * tok_bytes + chunk_off;
+                    }
+                    kb[u] = load_stream(kp + o);
+                    vb[u] = load_stream(vp + o);
+                }
             }
         };
-        auto compute = [&](const uint4 (&kb)[U], const uint4 (&vb)[U], int j) {
+        // Online-softmax update with the 16 tokens of step j.
+        auto compute = [&]<bool MASKED>(const vec4 (&kb)[U], const vec4 (&vb)[U], int j) {
             float sc[U][G];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool valid = ctb + j * kStepTokens + u * R + rg < cte;
+                const bool valid = !MASKED || ctb + j * kStepTokens + u * R + rg < cte;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     float x = group_sum<LPR>(E::dot(qv[g], kb[u])) * a.qk_scale;
@@ -301,20 +386,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
             }
         };
 
+        // Full steps: wave w takes steps w, w + 4, ...  The next step's loads
+        // are always issued before the current step is computed, with no
+        // conditional loads inside the loop, so exactly one step of loads is
+        // outstanding while a step is computed.
+        vec4 ka[U], va[U], kb2[U], vb2[U];
         int j = wave;
-        if (j < nsteps) {
-            uint4 ka[U], va[U], kb2[U], vb2[U];
-            load(ka, va, j);
-            while (true) {
-                if (j + kWaves < nsteps) load(kb2, vb2, j + kWaves);
-                compute(ka, va, j);
-                j += kWaves;
-                if (j >= nsteps) break;
-                if (j + kWaves < nsteps) load(ka, va, j + kWaves);
-                compute(kb2, vb2, j);
-                j += kWaves;
-                if (j >= nsteps) break;
+        if (j < nfull) {
+            issue.template operator()<false>(ka, va, j);
+            while (j + 2 * kWaves < nfull) {
+                issue.template operator()<false>(kb2, vb2, j + kWaves);
+                compute.template operator()<false>(ka, va, j);
+                issue.template operator()<false>(ka, va, j + 2 * kWaves);
+                compute.template operator()<false>(kb2, vb2, j + kWaves);
+                j += 2 * kWaves;
             }
+            if (j + kWaves < nfull) {
+                issue.template operator()<false>(kb2, vb2, j + kWaves);
+                compute.template operator()<false>(ka, va, j);
+                compute.template operator()<false>(kb2, vb2, j + kWaves);
+            } else {
+                compute.template operator()<false>(ka, va, j);
+            }
+        }
+        // The partly filled last step goes to the wave whose turn it is.
+        if (tail && wave == nfull % kWaves) {
+            issue.template operator()<true>(ka, va, nfull);
+            compute.template operator()<true>(ka, va, nfull);
         }
     }
 
@@ -423,23 +521,37 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.ws_acc = l.PS ? l.ws : nullptr;
     a.ws_ml = l.PS ? l.ws + units * l.D : nullptr;
     a.qk_scale = l.scale * kLog2e;
+    a.S = l.S;
     a.Hq = l.Hq;
     a.Hkv = l.Hkv;
     a.NB = l.NB;
     a.MBS = l.MBS;
+    const int B = l.dense ? kStepTokens : l.B;
     int lb = 0;
-    while ((1 << lb) < (l.dense ? kStepTokens : l.B)) ++lb;
+    while ((1 << lb) < B) ++lb;
     a.log2B = lb;
     a.max_ctx = l.max_ctx;
     a.PS = l.PS;
     a.P = l.P;
-    a.row_bytes = (int64_t)l.Hkv * D * sizeof(T);
-    a.pos_stride = l.pos_stride;
+    a.rank = (l.S > 1 && l.S <= kRankMaxSeqs) ? 1 : 0;
+    const int64_t row = (int64_t)D * sizeof(T);        // one head's row
+    const int64_t span = l.dense ? l.pos_stride : B;   // tokens per block / per sequence
+    if (l.layout == 0) {  // token-major: [..., tokens, Hkv, D]
+        a.tok_bytes = row * l.Hkv;
+        a.head_bytes = row;
+    } else {              // head-major: [..., Hkv, tokens, D]
+        a.tok_bytes = row;
+        a.head_bytes = row * span;
+    }
+    a.blk_bytes = l.dense ? 0 : row * l.Hkv * B;
+    a.seq_bytes = l.dense ? row * l.Hkv * l.pos_stride : 0;
     dim3 grid((unsigned)((int64_t)l.S * l.Hkv), (unsigned)l.P, 1);
     if (l.dense)
-        hipLaunchKernelGGL((decode_kernel<T, D, G, true>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), grid, dim3(kThreads), 0, st, a);
+    else if (l.B >= kStepTokens)
+        hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedWide>), grid, dim3(kThreads), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_kernel<T, D, G, false>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedNarrow>), grid, dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || l.PS == 0) return e;
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)l.S * l.Hq)), dim3(D), 0, st,
@@ -480,49 +592,63 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
 
 // ---------------------------------------------------------------- cache_write
 
-// One flat range of 16-byte vectors: token i's K row, then its V row.  A
-// vector goes to row ``slot`` of the pool (slot = block * B + offset, which
-// is the row index of the [NB, B, Hkv, D] layout).  Out-of-range slots are
-// skipped ([Kwon] §3.4 "Kernel-Level Optimizations", item 1).
+// One flat range of 16-byte vectors: token i's K rows, then its V rows, each
+// [Hkv, D] in the source.  Vector w of token i belongs to kv head g = w / rv
+// and goes to block slot / B, offset slot % B of that head in the pool
+// layout given by the strides.  Out-of-range slots are skipped ([Kwon] §3.4
+// "Kernel-Level Optimizations", item 1: one fused launch writes every new
+// token to the block and slot the scheduler names).
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(
-    const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new, uint4 *__restrict__ k_cache,
-    uint4 *__restrict__ v_cache, const int32_t *__restrict__ slots, int64_t total, int64_t rv,
-    int64_t num_slots) {
+    const vec4 *__restrict__ k_new, const vec4 *__restrict__ v_new, char *__restrict__ k_cache,
+    char *__restrict__ v_cache, const int32_t *__restrict__ slots, int64_t total, int64_t rv,
+    int32_t hkv, int32_t log2B, int64_t num_slots, int64_t blk_bytes, int64_t tok_bytes,
+    int64_t head_bytes) {
+    const int64_t per_tensor = (int64_t)hkv * rv;    // vectors of K (or V) per token
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
-        const int64_t i = idx / (2 * rv);
-        const int64_t rem = idx - i * 2 * rv;
-        const bool is_v = rem >= rv;
-        const int64_t w = is_v ? rem - rv : rem;
+        const int64_t i = idx / (2 * per_tensor);
+        int64_t w = idx - i * 2 * per_tensor;
+        const bool is_v = w >= per_tensor;
+        if (is_v) w -= per_tensor;
         const int32_t slot = slots[i];
         if (slot < 0 || slot >= num_slots) continue;
-        const uint4 x = is_v ? v_new[i * rv + w] : k_new[i * rv + w];
-        uint4 *dst = is_v ? v_cache : k_cache;
-        dst[(int64_t)slot * rv + w] = x;
+        const int64_t g = w / rv, x = w - g * rv;
+        const int64_t dst = (int64_t)(slot >> log2B) * blk_bytes +
+                            (int64_t)(slot & ((1 << log2B) - 1)) * tok_bytes + g * head_bytes +
+                            x * 16;
+        const vec4 val = is_v ? v_new[i * per_tensor + w] : k_new[i * per_tensor + w];
+        *reinterpret_cast<vec4 *>((is_v ? v_cache : k_cache) + dst) = val;
     }
 }
 
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                       const int32_t *slots, int32_t n, int64_t num_slots, int64_t row_bytes,
-                       void *stream) {
-    const int64_t rv = row_bytes / 16;
-    const int64_t total = (int64_t)n * 2 * rv;
+                       const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
+                       int32_t hkv, int64_t row_bytes, int32_t layout, void *stream) {
+    const int64_t rv = row_bytes / 16;  // vectors per head row
+    const int64_t total = (int64_t)n * 2 * hkv * rv;
+    int log2B = 0;
+    while ((1 << log2B) < block_size) ++log2B;
+    const int64_t blk_bytes = row_bytes * hkv * block_size;
+    const int64_t tok_bytes = layout == 0 ? row_bytes * hkv : row_bytes;
+    const int64_t head_bytes = layout == 0 ? row_bytes : row_bytes * block_size;
     int64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, (const uint4 *)k_new, (const uint4 *)v_new,
-                       (uint4 *)k_cache, (uint4 *)v_cache, slots, total, rv, num_slots);
+                       (hipStream_t)stream, (const vec4 *)k_new, (const vec4 *)v_new,
+                       (char *)k_cache, (char *)v_cache, slots, total, rv, hkv, log2B,
+                       (int64_t)num_blocks * block_size, blk_bytes, tok_bytes, head_bytes);
     return (int)hipGetLastError();
 }
 
 // ---------------------------------------------------------------- copy_blocks
 
 // Whole-block copies for every (src, dst) pair, K then V, in one launch
-// ([Kwon] §3.4 "Kernel-Level Optimizations", item 3).  Pairs naming a block
-// outside [0, NB) are skipped.
+// ([Kwon] §3.4 "Kernel-Level Optimizations", item 3).  A block is one
+// contiguous range in either pool layout.  Pairs naming a block outside
+// [0, NB) are skipped.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache, const int32_t *__restrict__ pairs,
+    vec4 *__restrict__ k_cache, vec4 *__restrict__ v_cache, const int32_t *__restrict__ pairs,
     int64_t total, int64_t bv, int32_t num_blocks) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
@@ -532,7 +658,7 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
         const int64_t w = is_v ? rem - bv : rem;
         const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
         if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-        uint4 *pool = is_v ? v_cache : k_cache;
+        vec4 *pool = is_v ? v_cache : k_cache;
         pool[(int64_t)dst * bv + w] = pool[(int64_t)src * bv + w];
     }
 }
@@ -545,7 +671,7 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, (uint4 *)k_cache, (uint4 *)v_cache, pairs, total, bv,
+                       (hipStream_t)stream, (vec4 *)k_cache, (vec4 *)v_cache, pairs, total, bv,
                        num_blocks);
     return (int)hipGetLastError();
 }
@@ -553,8 +679,9 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32
 const char *hip_error_name(int err) { return hipGetErrorName((hipError_t)err); }
 
 const char *kernel_build_info() {
-    return "gfx950; decode: 256 threads (4 wave64), 16-token wave steps, LDS block table, "
-           "G in 1..8, D in {64,128}, fp32/fp16/bf16; cache_write / copy_blocks: 16-byte vectors";
+    return "gfx950; decode: 256 threads (4 wave64), 16-token wave steps, non-temporal K/V loads, "
+           "LDS block table, longest-first order up to 256 sequences, G in 1..8, D in {64,128}, "
+           "fp32/fp16/bf16, token- or head-major blocks; cache_write / copy_blocks: 16-byte vectors";
 }
 
 }  // namespace pa

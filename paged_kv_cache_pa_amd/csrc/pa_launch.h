@@ -21,6 +21,7 @@ struct DecodeLaunch {
     int32_t PS;              // 0 = no split, else partition size (tokens)
     int32_t P;               // number of partitions (grid z), >= 1
     int64_t pos_stride;      // dense only: max_seq_len
+    int32_t layout;          // 0 token-major, 1 head-major
     bool dense;
 };
 
@@ -28,8 +29,8 @@ struct DecodeLaunch {
 int launch_decode(const DecodeLaunch &l, void *stream);
 
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                       const int32_t *slots, int32_t n, int64_t num_slots, int64_t row_bytes,
-                       void *stream);
+                       const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
+                       int32_t hkv, int64_t row_bytes, int32_t layout, void *stream);
 
 int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t n,
                        int32_t num_blocks, int64_t block_bytes, void *stream);

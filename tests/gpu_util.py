@@ -44,22 +44,35 @@ def empty_out(p: W.Paged):
     return torch.full(p.q.shape, float("nan"), dtype=torch_dtype(p.dtype), device=dev())
 
 
-def upload(p: W.Paged):
-    """q, k_cache, v_cache, block_tables, context_lens on the device."""
-    return (to_dev(p.q, p.dtype), to_dev(p.k_cache, p.dtype), to_dev(p.v_cache, p.dtype),
-            to_dev(p.block_tables), to_dev(p.context_lens))
+def head_major(a: np.ndarray) -> np.ndarray:
+    """[X, tokens, Hkv, D] -> [X, Hkv, tokens, D]."""
+    return np.ascontiguousarray(np.swapaxes(a, 1, 2))
 
 
-def run_decode(p: W.Paged, partition_size=None, max_context_len=None, tensors=None):
+def in_layout(a: np.ndarray, layout: str) -> np.ndarray:
+    return a if layout == "NHD" else head_major(a)
+
+
+def upload(p: W.Paged, layout="NHD"):
+    """q, k_cache, v_cache, block_tables, context_lens on the device; the pool
+    in the requested layout (the generators build token-major pools)."""
+    return (to_dev(p.q, p.dtype), to_dev(in_layout(p.k_cache, layout), p.dtype),
+            to_dev(in_layout(p.v_cache, layout), p.dtype), to_dev(p.block_tables),
+            to_dev(p.context_lens))
+
+
+def run_decode(p: W.Paged, partition_size=None, max_context_len=None, tensors=None,
+               layout="NHD"):
     import torch
 
     import paged_kv_cache_pa_amd as pa
 
-    q, k, v, bt, cl = tensors or upload(p)
+    q, k, v, bt, cl = tensors or upload(p, layout)
     out = empty_out(p)
     mcl = int(p.context_lens.max(initial=0)) if max_context_len is None else max_context_len
     ps = p.partition_size if partition_size is None else partition_size
-    pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl, partition_size=ps)
+    pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl, partition_size=ps,
+                 layout=layout)
     torch.cuda.synchronize()
     return to_host(out, p.dtype)
 

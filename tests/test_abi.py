@@ -50,7 +50,7 @@ def test_status_strings(L):
 def params(**kw):
     base = dict(num_seqs=4, num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
                 max_blocks_per_seq=7, num_blocks=64, max_context_len=112, partition_size=0,
-                dtype=0)
+                dtype=0, layout=0)
     base.update(kw)
     return DecodeParams(*[base[f] for f, _ in DecodeParams._fields_])
 
@@ -81,7 +81,9 @@ def decode(L, p, q=None, k=None, v=None, t=None, c=None, out=None, ws=None, nbyt
     (dict(max_blocks_per_seq=0), SHAPE), (dict(num_blocks=0), SHAPE),
     (dict(max_context_len=-1), SHAPE), (dict(max_context_len=7 * 16 + 1), SHAPE),
     (dict(partition_size=8), SHAPE), (dict(partition_size=-16), SHAPE),
+    (dict(layout=2), SHAPE), (dict(layout=-1), SHAPE),
     (dict(head_dim=96), UNSUP), (dict(head_dim=256), UNSUP),
+    (dict(num_kv_heads=1 << 20, num_q_heads=1 << 20), UNSUP),
     (dict(num_q_heads=18, num_kv_heads=2), UNSUP),
 ])
 def test_decode_rejects_bad_shapes(L, kw, code):
@@ -150,7 +152,7 @@ def test_dense_checks(L):
 
 
 def cparams(**kw):
-    base = dict(num_blocks=64, block_size=16, num_kv_heads=8, head_dim=64, dtype=0)
+    base = dict(num_blocks=64, block_size=16, num_kv_heads=8, head_dim=64, dtype=0, layout=0)
     base.update(kw)
     return CacheParams(*[base[f] for f, _ in CacheParams._fields_])
 
@@ -159,6 +161,7 @@ def cparams(**kw):
     (dict(dtype=5), DTYPE), (dict(num_blocks=0), SHAPE), (dict(block_size=3), SHAPE),
     (dict(num_kv_heads=0), SHAPE), (dict(head_dim=0), SHAPE),
     (dict(head_dim=6, dtype=1), SHAPE),   # 12-byte rows cannot be moved as 16-byte vectors
+    (dict(layout=7), SHAPE),
 ])
 def test_cache_write_and_copy_reject_bad_params(L, kw, code):
     b = Buf()

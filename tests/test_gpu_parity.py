@@ -11,10 +11,11 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import empty_out, f64, run_decode, to_dev, to_host, upload
+from gpu_util import empty_out, f64, head_major, in_layout, run_decode, to_dev, to_host, upload
 from helpers import assert_fp_close, same_bits
 
 pytestmark = pytest.mark.gpu
+LAYOUTS = ["NHD", "HND"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -44,84 +45,97 @@ def check(p, got, ref, what, units=None):
 # ---------------------------------------------------------------- the configurations
 
 
-def test_config1_write_then_decode():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_config1_write_then_decode(layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
 
     p = W.config1()
-    q, k, v, bt, cl = upload(p)
-    pa.pa_cache_write(to_dev(p.k_new), to_dev(p.v_new), k, v, to_dev(p.slot_mapping))
+    q, k, v, bt, cl = upload(p, layout)
+    pa.pa_cache_write(to_dev(p.k_new), to_dev(p.v_new), k, v, to_dev(p.slot_mapping), layout=layout)
     torch.cuda.synchronize()
-    kc, vc = oracle.cache_write(p.k_new, p.v_new, p.k_cache, p.v_cache, p.slot_mapping, "f32")
+    kc, vc = oracle.cache_write(p.k_new, p.v_new, in_layout(p.k_cache, layout),
+                                in_layout(p.v_cache, layout), p.slot_mapping, "f32", layout=layout)
     assert same_bits(to_host(k, "f32"), kc) and same_bits(to_host(v, "f32"), vc)
+    ref = oracle.decode(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, "f32", layout=layout)
     pw = W.Paged("f32", p.q, kc, vc, p.block_tables, p.context_lens, p.scale, 16)
-    ref = ref_decode(pw)
     for ps in (0, 16, 32, 64):
-        got = run_decode(pw, partition_size=ps, tensors=(q, k, v, bt, cl))
-        check(pw, got, ref, f"config1 partition {ps}")
+        got = run_decode(pw, partition_size=ps, tensors=(q, k, v, bt, cl), layout=layout)
+        check(pw, got, ref, f"config1 {layout} partition {ps}")
 
 
-def test_config2_full():
+@pytest.fixture(scope="module")
+def cfg2():
     p = W.config2()
-    ref = ref_decode(p)
-    t = upload(p)
+    return p, ref_decode(p)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_config2_full(cfg2, layout):
+    p, ref = cfg2
+    t = upload(p, layout)
     outs = {}
     for ps in (0, 256, 512):
-        outs[ps] = run_decode(p, partition_size=ps, tensors=t)
-        check(p, outs[ps], ref, f"config2 partition {ps}")
+        outs[ps] = run_decode(p, partition_size=ps, tensors=t, layout=layout)
+        check(p, outs[ps], ref, f"config2 {layout} partition {ps}")
     # with 1024 <= partition, one partition covers every sequence: same bits as no split
-    assert same_bits(run_decode(p, partition_size=2048, tensors=t), outs[0])
+    assert same_bits(run_decode(p, partition_size=2048, tensors=t, layout=layout), outs[0])
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("batch,ctx", [(8, 64), (8, 256), (32, 256), (8, 1024), (8, 2048), (32, 64),
                                        (128, 64)])
-def test_config3_paged_vs_dense(batch, ctx):
+def test_config3_paged_vs_dense(batch, ctx, layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
 
     p = W.config3(batch, ctx)
     ref = oracle.decode_dense(p.q, p.k_dense, p.v_dense, p.context_lens, p.scale, "f16")
-    t = upload(p)
-    got = run_decode(p, partition_size=0, tensors=t)
-    check(p, got, ref, f"config3 paged {batch}x{ctx}")
+    t = upload(p, layout)
+    got = run_decode(p, partition_size=0, tensors=t, layout=layout)
+    check(p, got, ref, f"config3 paged {layout} {batch}x{ctx}")
     out = empty_out(p)
-    pa.pa_decode_dense(t[0], to_dev(p.k_dense), to_dev(p.v_dense), t[4], p.scale, out,
-                       max_context_len=ctx)
+    pa.pa_decode_dense(t[0], to_dev(in_layout(p.k_dense, layout)), to_dev(in_layout(p.v_dense, layout)),
+                       t[4], p.scale, out, max_context_len=ctx, layout=layout)
     torch.cuda.synchronize()
     assert same_bits(to_host(out, "f16"), got), "paged and dense differ"
 
 
-def test_config4_cow_write_decode():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_config4_cow_write_decode(layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
 
     sc = W.config4()
     p = sc.paged
-    q, k, v, bt, cl = upload(p)
-    pa.pa_copy_blocks(k, v, to_dev(p.block_pairs))
-    pa.pa_cache_write(to_dev(p.k_new, "f16"), to_dev(p.v_new, "f16"), k, v, to_dev(p.slot_mapping))
+    q, k, v, bt, cl = upload(p, layout)
+    pa.pa_copy_blocks(k, v, to_dev(p.block_pairs), layout=layout)
+    pa.pa_cache_write(to_dev(p.k_new, "f16"), to_dev(p.v_new, "f16"), k, v, to_dev(p.slot_mapping),
+                      layout=layout)
     torch.cuda.synchronize()
-    kc, vc = oracle.copy_blocks(p.k_cache, p.v_cache, p.block_pairs, "f16")
-    kc, vc = oracle.cache_write(p.k_new, p.v_new, kc, vc, p.slot_mapping, "f16")
+    kc, vc = oracle.copy_blocks(in_layout(p.k_cache, layout), in_layout(p.v_cache, layout),
+                                p.block_pairs, "f16", layout=layout)
+    kc, vc = oracle.cache_write(p.k_new, p.v_new, kc, vc, p.slot_mapping, "f16", layout=layout)
     assert same_bits(to_host(k, "f16"), kc) and same_bits(to_host(v, "f16"), vc)
+    ref = oracle.decode(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, "f16", layout=layout)
     pw = W.Paged("f16", p.q, kc, vc, p.block_tables, p.context_lens, p.scale, 16)
-    ref = ref_decode(pw)
     for ps in (0, 256):
-        got = run_decode(pw, partition_size=ps, tensors=(q, k, v, bt, cl))
-        check(pw, got, ref, f"config4 partition {ps}")
+        got = run_decode(pw, partition_size=ps, tensors=(q, k, v, bt, cl), layout=layout)
+        check(pw, got, ref, f"config4 {layout} partition {ps}")
 
 
-def test_config5_gqa_split():
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_config5_gqa_split(layout):
     p = W.config5()
     ref = ref_decode(p)
-    t = upload(p)
-    got = run_decode(p, partition_size=512, tensors=t)
-    check(p, got, ref, "config5 partition 512")
-    got0 = run_decode(p, partition_size=0, tensors=t)
-    check(p, got0, ref, "config5 no split")
+    t = upload(p, layout)
+    got = run_decode(p, partition_size=512, tensors=t, layout=layout)
+    check(p, got, ref, f"config5 {layout} partition 512")
+    got0 = run_decode(p, partition_size=0, tensors=t, layout=layout)
+    check(p, got0, ref, f"config5 {layout} no split")
 
 
 @pytest.mark.parametrize("n", [4096, 10000, 12000, 16384])
@@ -195,20 +209,22 @@ EDGE_LENS = [0, 1, 15, 16, 17, 31, 32, 33, 511, 512, 513, 1000]
                                             ("f16", 8, 8, 128), ("f16", 6, 3, 64),
                                             ("bf16", 12, 2, 128), ("bf16", 8, 1, 64)])
 @pytest.mark.parametrize("ps", [0, 32, 512])
-def test_edge_lengths(dtype, hq, hkv, d, ps):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_edge_lengths(dtype, hq, hkv, d, ps, layout):
     p = W.random_paged(21, dtype, EDGE_LENS, hq, hkv, d)
-    got = run_decode(p, partition_size=ps)
-    check(p, got, ref_decode(p), f"edge lengths {dtype} {hq}/{hkv} D{d} ps{ps}")
+    got = run_decode(p, partition_size=ps, layout=layout)
+    check(p, got, ref_decode(p), f"edge lengths {layout} {dtype} {hq}/{hkv} D{d} ps{ps}")
     assert (f64(got[0], dtype) == 0).all(), "empty sequence must give zeros"
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128, 256])
-def test_block_sizes(B):
+def test_block_sizes(B, layout):
     p = W.random_paged(22, "f16", [1, B - 1 if B > 1 else 1, B, B + 1, 3 * B + 5, 700], 4, 2, 128,
                        block_size=B)
     for ps in (0, max(B, 256)):
-        got = run_decode(p, partition_size=ps)
-        check(p, got, ref_decode(p), f"block size {B} ps {ps}")
+        got = run_decode(p, partition_size=ps, layout=layout)
+        check(p, got, ref_decode(p), f"block size {B} {layout} ps {ps}")
 
 
 @pytest.mark.parametrize("G", range(1, 9))
@@ -233,18 +249,19 @@ def test_single_token_is_exact(dtype):
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
 @pytest.mark.parametrize("ps", [0, 32])
-def test_paged_equals_dense_bitwise(dtype, ps):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paged_equals_dense_bitwise(dtype, ps, layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
 
     p = W.random_with_dense(25, dtype, [0, 1, 16, 17, 100, 333], 8, 4, 128)
     smax = p.k_dense.shape[1]
-    paged = run_decode(p, partition_size=ps, max_context_len=smax)
+    paged = run_decode(p, partition_size=ps, max_context_len=smax, layout=layout)
     out = empty_out(p)
-    pa.pa_decode_dense(to_dev(p.q, dtype), to_dev(p.k_dense, dtype), to_dev(p.v_dense, dtype),
-                       to_dev(p.context_lens), p.scale, out, max_context_len=smax,
-                       partition_size=ps)
+    pa.pa_decode_dense(to_dev(p.q, dtype), to_dev(in_layout(p.k_dense, layout), dtype),
+                       to_dev(in_layout(p.v_dense, layout), dtype), to_dev(p.context_lens),
+                       p.scale, out, max_context_len=smax, partition_size=ps, layout=layout)
     torch.cuda.synchronize()
     dense = to_host(out, dtype)
     assert same_bits(paged, dense)
@@ -284,7 +301,8 @@ def test_poison_is_never_read():
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
-def test_cache_write_bit_exact(dtype):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_cache_write_bit_exact(dtype, layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -292,14 +310,15 @@ def test_cache_write_bit_exact(dtype):
     rng = np.random.default_rng(29)
     NB, B, H, D = 40, 16, 4, 64
     k0, v0 = W.nan_fill((NB, B, H, D), dtype), W.nan_fill((NB, B, H, D), dtype)
+    k0, v0 = in_layout(k0, layout), in_layout(v0, layout)
     N = 300
     slots = rng.permutation(NB * B)[:N].astype(np.int32)
     slots[::7] = -1
     kn, vn = W.randn(rng, (N, H, D), dtype), W.randn(rng, (N, H, D), dtype)
     k, v = to_dev(k0, dtype), to_dev(v0, dtype)
-    pa.pa_cache_write(to_dev(kn, dtype), to_dev(vn, dtype), k, v, to_dev(slots))
+    pa.pa_cache_write(to_dev(kn, dtype), to_dev(vn, dtype), k, v, to_dev(slots), layout=layout)
     torch.cuda.synchronize()
-    kc, vc = oracle.cache_write(kn, vn, k0, v0, slots, dtype)
+    kc, vc = oracle.cache_write(kn, vn, k0, v0, slots, dtype, layout=layout)
     assert same_bits(to_host(k, dtype), kc) and same_bits(to_host(v, dtype), vc)
 
 
@@ -352,6 +371,19 @@ def test_share_fixture_end_to_end(golden):
     p = W.Paged("bf16", q, kc, vc, tab, np.full(g["samples"], N, np.int32), 0.088, B)
     got = run_decode(p, tensors=(to_dev(q, "bf16"), k, v, to_dev(tab), to_dev(p.context_lens)))
     check(p, got, ref_decode(p), "share fixture")
+
+
+@pytest.mark.parametrize("S", [1, 2, 255, 256, 257, 600])
+def test_batch_sizes_and_scheduling(S):
+    """Longest-first order is used up to 256 sequences, natural order above;
+    both must give every row, ties included."""
+    rng = np.random.default_rng(40 + S)
+    lens = rng.integers(0, 90, size=S)
+    lens[::5] = 33  # many ties
+    p = W.random_paged(41, "bf16", lens, 4, 2, 64, extra_blocks=2)
+    for layout in LAYOUTS:
+        check(p, run_decode(p, layout=layout), ref_decode(p), f"S={S} {layout}")
+    check(p, run_decode(p, partition_size=32), ref_decode(p), f"S={S} split")
 
 
 def test_side_stream():

@@ -361,6 +361,35 @@ def test_paged_equals_dense(dtype):
     assert same_bits(out, outd)
 
 
+def to_head_major(a):
+    """[X, tokens, Hkv, D] -> [X, Hkv, tokens, D] (numpy transpose)."""
+    return np.ascontiguousarray(np.swapaxes(a, 1, 2))
+
+
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_head_major_layout_matches_transpose(dtype):
+    """The head-major pool holds the same values, transposed inside each
+    block: decode, dense decode and cache_write must agree bitwise."""
+    p = W.random_with_dense(33, dtype, [7, 0, 40, 95], 6, 3, 32, block_size=8)
+    ref = oracle.decode(p.q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, dtype)
+    hm = oracle.decode(p.q, to_head_major(p.k_cache), to_head_major(p.v_cache), p.block_tables,
+                       p.context_lens, p.scale, dtype, layout="HND")
+    assert same_bits(ref, hm)
+    dh = oracle.decode_dense(p.q, to_head_major(p.k_dense), to_head_major(p.v_dense),
+                             p.context_lens, p.scale, dtype, layout="HND")
+    assert same_bits(ref, dh)
+    sp = oracle.decode_split(p.q, to_head_major(p.k_cache), to_head_major(p.v_cache),
+                             p.block_tables, p.context_lens, p.scale, dtype, 16, layout="HND")
+    assert np.allclose(sp, ref, rtol=1e-13, atol=1e-14)
+    rng = np.random.default_rng(34)
+    slots = rng.permutation(p.num_blocks * 8)[:20].astype(np.int32)
+    kn, vn = W.randn(rng, (20, 3, 32), dtype), W.randn(rng, (20, 3, 32), dtype)
+    kc, vc = oracle.cache_write(kn, vn, p.k_cache, p.v_cache, slots, dtype)
+    kh, vh = oracle.cache_write(kn, vn, to_head_major(p.k_cache), to_head_major(p.v_cache), slots,
+                                dtype, layout="HND")
+    assert same_bits(to_head_major(kc), kh) and same_bits(to_head_major(vc), vh)
+
+
 @pytest.mark.parametrize("P", [16, 32, 48, 512])
 def test_split_merge_identity(P):
     p = W.random_paged(14, "bf16", [0, 1, 15, 16, 17, 47, 48, 49, 300, 700], 6, 2, 32)

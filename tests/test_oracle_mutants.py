@@ -23,9 +23,11 @@ MUTANTS = [
     ("block_index_transposed", "int32_t b = row[t / B];", "int32_t b = row[t % B];",
      ["test_fig6_slots_and_gather"]),
     ("offset_transposed",
-     "size_t base = (((size_t)b * B + (size_t)(t % B)) * Hkv + g) * D;",
-     "size_t base = (((size_t)b * B + (size_t)((t / B) % B)) * Hkv + g) * D;",
+     "size_t base = pool_index(layout, (size_t)b, (size_t)(t % B), (size_t)g, B, Hkv, D);",
+     "size_t base = pool_index(layout, (size_t)b, (size_t)((t / B) % B), (size_t)g, B, Hkv, D);",
      ["test_fig6_slots_and_gather", "test_hand_weights"]),
+    ("head_major_swapped", "return ((b * Hkv + g) * B + o) * D;", "return ((b * B + o) * Hkv + g) * D;",
+     ["test_head_major_layout_matches_transpose"]),
     ("head_map_interleaved", "int s = units ? units[2 * u] : u / Hq;\n        int h = units ? units[2 * u + 1] : u % Hq;\n        int n = context_lens[s];\n        int g = h / G;\n        size_t nn = n > 0 ? (size_t)n : 1;\n        double *K = malloc(nn * D * sizeof(double));\n        double *V = malloc(nn * D * sizeof(double));\n        double *x = malloc(nn * sizeof(double));\n        double *qv = malloc((size_t)D * sizeof(double));\n        if (!K || !V || !x || !qv) {\n            err = -1;\n        } else {\n            const int32_t",
      "int s = units ? units[2 * u] : u / Hq;\n        int h = units ? units[2 * u + 1] : u % Hq;\n        int n = context_lens[s];\n        int g = h % Hkv;\n        size_t nn = n > 0 ? (size_t)n : 1;\n        double *K = malloc(nn * D * sizeof(double));\n        double *V = malloc(nn * D * sizeof(double));\n        double *x = malloc(nn * sizeof(double));\n        double *qv = malloc((size_t)D * sizeof(double));\n        if (!K || !V || !x || !qv) {\n            err = -1;\n        } else {\n            const int32_t",
      ["test_gqa_head_map_contiguous_groups"]),
@@ -33,8 +35,9 @@ MUTANTS = [
      ["test_half_widening_exhaustive"]),
     ("merge_sign", "double cp = exp(mp - Mn);", "double cp = exp(Mn - mp);",
      ["test_split_merge_identity"]),
-    ("write_offset", "size_t dst = ((size_t)(slot / B) * B + (size_t)(slot % B)) * row;",
-     "size_t dst = ((size_t)(slot / B) * B + (size_t)((slot + 1) % B)) * row;",
+    ("write_offset",
+     "size_t dst = pool_index(layout, (size_t)(slot / B), (size_t)(slot % B), (size_t)g,",
+     "size_t dst = pool_index(layout, (size_t)(slot / B), (size_t)((slot + 1) % B), (size_t)g,",
      ["test_fig6_slots_and_gather", "test_cache_write_matches_numpy_scatter"]),
     ("copy_direction", "memmove((char *)k_cache + dst, (const char *)k_cache + src, blk);",
      "memmove((char *)k_cache + src, (const char *)k_cache + dst, blk);",
