@@ -187,6 +187,129 @@ def copy_blocks_rate(rounds=15):
             "replicas": R}
 
 
+def _dev_pool(a, layout):
+    import torch
+
+    a = np.ascontiguousarray(np.swapaxes(a, 1, 2)) if layout == "HND" else a
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def _dev(a):
+    import torch
+
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sweep(rounds=10):
+    """Every configuration's kernels, timed over rotating replicas (one JSON
+    object per line; not the benchmark's contract line)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+    import workloads as W
+
+    st = torch.cuda.current_stream()
+
+    def emit(**kw):
+        print(json.dumps(kw), flush=True)
+
+    def time_decode(p, layout, ps, label, nbytes=None):
+        S, Hq, D = p.q.shape
+        e = W.ELEM_BYTES[p.dtype]
+        k0, v0 = _dev_pool(p.k_cache, layout), _dev_pool(p.v_cache, layout)
+        R = replicas_for(2 * k0.numel() * k0.element_size())
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+        q, bt, cl = _dev(p.q), _dev(p.block_tables), _dev(p.context_lens)
+        out = torch.empty_like(q)
+        mcl = int(p.context_lens.max())
+        params = pa.DecodeParams(S, Hq, p.num_kv_heads, D, p.block_size, p.max_blocks_per_seq,
+                                 p.num_blocks, mcl, ps, {"f32": 0, "f16": 1, "bf16": 2}[p.dtype],
+                                 pa.LAYOUTS[layout])
+        need = pa.pa_decode_workspace_size(params)
+        ws = torch.empty(max(1, need // 4), dtype=torch.float32, device="cuda")
+
+        def f(i):
+            k, v = pools[i % R]
+            pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl, partition_size=ps,
+                         workspace=ws, layout=layout)
+
+        for i in range(2 * R):
+            f(i)
+        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        b = nbytes or decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, e, p.block_size)
+        emit(config=label, kernel="pa_decode", layout=layout, partition=ps, us=round(t * 1e6, 2),
+             algorithmic_bytes=b, GB_s=round(b / t / 1e9, 1), frac=round(b / t / 8e12, 4),
+             kv_tokens_per_s=round(float(p.context_lens.sum()) / t, 1), replicas=R)
+        del pools
+        torch.cuda.empty_cache()
+
+    def time_write(p, layout, label):
+        k0, v0 = _dev_pool(p.k_cache, layout), _dev_pool(p.v_cache, layout)
+        R = replicas_for(2 * k0.numel() * k0.element_size())
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+        kn, vn, sm = _dev(p.k_new), _dev(p.v_new), _dev(p.slot_mapping)
+
+        def f(i):
+            k, v = pools[i % R]
+            pa.pa_cache_write(kn, vn, k, v, sm, layout=layout)
+
+        for i in range(R):
+            f(i)
+        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        N = p.slot_mapping.shape[0]
+        b = 2 * 2 * N * p.num_kv_heads * p.head_dim * W.ELEM_BYTES[p.dtype] + 4 * N
+        emit(config=label, kernel="pa_cache_write", layout=layout, tokens=N, us=round(t * 1e6, 2),
+             algorithmic_bytes=b, GB_s=round(b / t / 1e9, 1))
+        del pools
+        torch.cuda.empty_cache()
+
+    def time_copy(p, label):
+        k0, v0 = _dev(p.k_cache), _dev(p.v_cache)
+        R = replicas_for(2 * k0.numel() * k0.element_size())
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+        pairs = _dev(p.block_pairs)
+
+        def f(i):
+            k, v = pools[i % R]
+            pa.pa_copy_blocks(k, v, pairs)
+
+        for i in range(R):
+            f(i)
+        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        n = p.block_pairs.shape[0]
+        b = 2 * 2 * n * p.block_size * p.num_kv_heads * p.head_dim * W.ELEM_BYTES[p.dtype] + 8 * n
+        emit(config=label, kernel="pa_copy_blocks", pairs=n, us=round(t * 1e6, 2),
+             algorithmic_bytes=b, GB_s=round(b / t / 1e9, 1))
+        del pools
+        torch.cuda.empty_cache()
+
+    c1 = W.config1(poison=False)
+    for lay in ("NHD", "HND"):
+        time_write(c1, lay, "c1")
+        time_decode(c1, lay, 0, "c1")
+    c2 = W.config2()
+    for lay in ("HND", "NHD"):
+        for ps in (0, 512):
+            time_decode(c2, lay, ps, "c2")
+    sc = W.config4(poison=False)
+    time_copy(sc.paged, "c4")
+    for lay in ("HND", "NHD"):
+        time_write(sc.paged, lay, "c4")
+        time_decode(sc.paged, lay, 0, "c4")
+    c5 = W.config5()
+    for lay in ("HND", "NHD"):
+        for ps in (512, 256, 0):
+            time_decode(c5, lay, ps, "c5 mixed")
+    for n in W.CONFIG5_LENS:
+        time_decode(W.config5(uniform_len=n), "HND", 512, f"c5 uniform {n}")
+    for point, r in paged_dense_ratio(W.CONFIG3_POINTS, rounds=rounds).items():
+        emit(config="c3 " + point, kernel="pa_decode vs pa_decode_dense", **r)
+
+
 def cpu_baseline(p, budget_s=12.0, max_runs=200):
     """The fp64 oracle on the host cores, on the same batch: the whole batch,
     repeated for about ``budget_s`` seconds (at least 3 runs); median."""
@@ -377,6 +500,8 @@ def main():
                     help="skip the dense ratio, copy_blocks and CPU legs (for profiling runs)")
     ap.add_argument("--counters-run", action="store_true",
                     help="short run for rocprofv3 --pmc passes (decode launches + calibration copy)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every configuration's kernels (JSON lines, not the contract line)")
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
                     help="write profile summaries from rocprofv3 CSV output (no GPU needed)")
     args = ap.parse_args()
@@ -399,6 +524,9 @@ def main():
     pa.lib()  # fail loudly if the HIP library is missing
     if args.counters_run:
         counters_run(args)
+        return
+    if args.sweep:
+        sweep()
         return
     dev = torch.device("cuda:0")
     t_gen = time.time()

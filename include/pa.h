@@ -134,9 +134,9 @@ int pa_decode_workspace_size(const pa_decode_params *p, size_t *bytes);
  * the dtype (round to nearest even).
  *
  * q, k_cache, v_cache, block_tables, context_lens, out: device pointers.
- * workspace: device pointer to at least pa_decode_workspace_size() bytes
- * when that size is non-zero (may be NULL otherwise); its contents on entry
- * do not matter and are left unspecified.
+ * workspace: device pointer (16-byte aligned) to at least
+ * pa_decode_workspace_size() bytes when that size is non-zero (may be NULL
+ * otherwise); its contents on entry do not matter and are left unspecified.
  * Device-side conditions: 0 <= context_lens[s] <= max_context_len and
  * 0 <= block_tables[s][j] < num_blocks for j < ceil(n / B).  A longer
  * context is clamped to max_context_len (and to MBS * B); a table entry

@@ -79,7 +79,7 @@ int run_decode(const void *q, const void *k, const void *v, const int32_t *table
     const size_t need = workspace_bytes(p);
     if (need) {
         if (!ws || ws_bytes < need) return PA_ERR_WORKSPACE;
-        if ((uintptr_t)ws & 3u) return PA_ERR_ALIGN;
+        if (!aligned16(ws)) return PA_ERR_ALIGN;
     }
     pa::DecodeLaunch l;
     l.q = q;

@@ -58,8 +58,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
 typedef uint32_t vec4 __attribute__((ext_vector_type(4)));  // 16 bytes
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;       // cache_write / copy_blocks workgroups
+constexpr int kMaxWaves = 8;        // decode workgroups have 4 or 8 waves (chosen per launch)
 constexpr int kStepTokens = 16;     // tokens per wave step
 constexpr int kTableChunk = 1024;   // block-table entries staged in LDS at once
 constexpr int kRankMaxSeqs = 256;   // longest-first scheduling up to this batch
@@ -190,6 +190,7 @@ struct DecodeArgs {
     float qk_scale;  // scale * log2(e)
     int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, PS, P;
     int32_t rank;       // 1: longest-first sequence order (S <= kRankMaxSeqs)
+    int32_t spec_blocks;  // table entries a partition can need (fetched before its length)
     int64_t tok_bytes;  // bytes between consecutive tokens of one head
     int64_t head_bytes; // bytes between kv heads at a fixed token
     int64_t blk_bytes;  // paged: bytes per block
@@ -203,23 +204,86 @@ enum : int {
     kPagedNarrow = 2 // paged, B < 16: a step spans several blocks
 };
 
+__device__ __forceinline__ int clamp_len(int x, int max_ctx) {
+    return x < 0 ? 0 : (x > max_ctx ? max_ctx : x);
+}
+
+// Longest-first order: rank(t) = #{u : n_u > n_t} + #{u < t : n_u == n_t}.
+// Stages every clamped length in s_len and returns the sequence of rank
+// `want` (a permutation, so exactly one thread finds it).
+__device__ int rank_pick(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, int want, int tid,
+                         int nt_) {
+    for (int t = tid; t < a.S; t += nt_) s_len[t] = clamp_len(a.lens[t], a.max_ctx);
+    __syncthreads();
+    for (int t = tid; t < a.S; t += nt_) {
+        const int nt = s_len[t];
+        int r = 0;
+        for (int u = 0; u < a.S; ++u) {
+            const int nu = s_len[u];
+            r += (nu > nt) | ((nu == nt) & (u < t));
+        }
+        if (r == want) *s_pick = t;
+    }
+    __syncthreads();
+    return *s_pick;
+}
+
+// Block-table entries [b0, b0 + cnt) of one row into LDS, clamped into [0, NB).
+__device__ void stage_table(const int32_t *trow, int b0, int cnt, int NB, int32_t *s_tab, int tid,
+                            int nt_) {
+    for (int i = tid; i < cnt; i += nt_) {
+        const int32_t b = trow[b0 + i];
+        s_tab[i] = b < 0 ? 0 : (b >= NB ? NB - 1 : b);
+    }
+}
+
+// Which sequence a workgroup serves.  Without ranking, the first table chunk
+// does not depend on the context length, so it is fetched together with the
+// length instead of after it (*staged = true; a barrier publishes it).
+template <int MODE>
+__device__ void pick_work(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, int32_t *s_tab,
+                          int tid, int nt_, int &s, int &n, bool &staged) {
+    const int want = blockIdx.x / a.Hkv;
+    staged = false;
+    if (a.rank) {
+        s = rank_pick(a, s_len, s_pick, want, tid, nt_);
+        n = s_len[s];
+        return;
+    }
+    s = want;
+    if constexpr (MODE != kDense) {
+        const int b0 = (a.PS ? (int)blockIdx.y * a.PS : 0) >> a.log2B;
+        const int cnt = min(min(kTableChunk, a.spec_blocks), a.MBS - b0);
+        stage_table(a.tables + (int64_t)s * a.MBS, b0, cnt, a.NB, s_tab, tid, nt_);
+        staged = true;
+    }
+    n = clamp_len(a.lens[s], a.max_ctx);
+}
+
+// fp32 rows need twice the registers per token, so fp32 workgroups keep 4 waves.
+template <typename T>
+constexpr int max_waves() { return sizeof(T) == 4 ? 4 : kMaxWaves; }
+
 template <typename T, int D, int G, int MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs a) {
     using E = Elem<T>;
     constexpr int EPL = E::kEPL;
     constexpr int LPR = D / EPL;               // lanes per token row
     constexpr int R = 64 / LPR;                // rows per wave load
     constexpr int U = kStepTokens / R;         // loads per step (K and V each)
-    constexpr int RED = kWaves * G * (D + 2);  // cross-wave merge floats
-    constexpr int SMEM = RED > kTableChunk ? RED : kTableChunk;
     static_assert(LPR == 8 || LPR == 16 || LPR == 32, "row must be 128, 256 or 512 bytes");
     static_assert(U * R == kStepTokens, "step shape");
 
-    __shared__ float smem[SMEM];
+    // Dynamic LDS (sized by the launcher): the block-table chunk during the
+    // loop, then the cross-wave merge buffer [waves][G][D + 2].
+    extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+    float *smem = reinterpret_cast<float *>(dyn_smem);
     __shared__ int32_t s_len[kRankMaxSeqs];
     __shared__ int32_t s_pick;
     int32_t *s_tab = reinterpret_cast<int32_t *>(smem);
 
+    const int nthr = blockDim.x;   // 64 * waves
+    const int nw = nthr >> 6;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -229,48 +293,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int part = blockIdx.y;
 
     int s, n;
-    if (a.rank) {
-        // Longest-first: rank(t) = #{u : n_u > n_t} + #{u < t : n_u == n_t};
-        // this workgroup serves the sequence of rank blockIdx.x / Hkv.
-        for (int t = tid; t < a.S; t += kThreads) {
-            const int x = a.lens[t];
-            s_len[t] = x < 0 ? 0 : (x > a.max_ctx ? a.max_ctx : x);
-        }
-        __syncthreads();
-        const int want = blockIdx.x / a.Hkv;
-        for (int t = tid; t < a.S; t += kThreads) {
-            const int nt = s_len[t];
-            int r = 0;
-            for (int u = 0; u < a.S; ++u) {
-                const int nu = s_len[u];
-                r += (nu > nt) | ((nu == nt) & (u < t));
-            }
-            if (r == want) s_pick = t;
-        }
-        __syncthreads();
-        s = s_pick;
-        n = s_len[s];
-    } else {
-        s = blockIdx.x / a.Hkv;
-        n = a.lens[s];
-        n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-    }
+    bool staged;
+    pick_work<MODE>(a, s_len, &s_pick, s_tab, tid, nthr, s, n, staged);
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;  // first query head of the group
 
-    if (tb >= te) {
-        // Only an empty sequence reaches here with part == 0: its row is zero.
-        if (part == 0)
-            for (int i = tid; i < G * D; i += kThreads) E::store(a.out, qrow0 * D + i, 0.0f);
-        return;
-    }
-
-    // q for the G heads of the group: this lane's 16-byte chunk, unscaled.
+    // q for the G heads of the group: this lane's 16-byte chunk, unscaled
+    // (issued before the length test so it overlaps the other first loads).
     vec4 qv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g)
         qv[g] = load_cached(a.q + ((qrow0 + g) * D + (int64_t)c * EPL) * sizeof(T));
+
+    if (tb >= te) {
+        // Only an empty sequence reaches here with part == 0: its row is zero.
+        if (part == 0)
+            for (int i = tid; i < G * D; i += nthr) E::store(a.out, qrow0 * D + i, 0.0f);
+        return;
+    }
 
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -302,13 +343,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         const int ctb = tb + cb * B;                 // first token of this chunk
         const int cte = min(te, ctb + cn * B);       // one past its last token
         if constexpr (MODE != kDense) {
-            __syncthreads();  // the previous chunk's readers are done
-            const int b0 = (tb >> a.log2B) + cb;
-            for (int i = tid; i < cn; i += kThreads) {
-                int32_t b = trow[b0 + i];
-                s_tab[i] = b < 0 ? 0 : (b >= a.NB ? a.NB - 1 : b);
+            __syncthreads();  // the previous chunk's readers are done / the first chunk is out
+            if (!(cb == 0 && staged)) {
+                stage_table(trow, (tb >> a.log2B) + cb, cn, a.NB, s_tab, tid, nthr);
+                __syncthreads();
             }
-            __syncthreads();
         }
         const int nfull = (cte - ctb) / kStepTokens;      // steps with 16 valid tokens
         const int tail = (cte - ctb) % kStepTokens;        // valid tokens of the last step
@@ -394,23 +433,26 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         int j = wave;
         if (j < nfull) {
             issue.template operator()<false>(ka, va, j);
-            while (j + 2 * kWaves < nfull) {
-                issue.template operator()<false>(kb2, vb2, j + kWaves);
+            while (j + 2 * nw < nfull) {
+                issue.template operator()<false>(kb2, vb2, j + nw);
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
                 compute.template operator()<false>(ka, va, j);
-                issue.template operator()<false>(ka, va, j + 2 * kWaves);
-                compute.template operator()<false>(kb2, vb2, j + kWaves);
-                j += 2 * kWaves;
+                issue.template operator()<false>(ka, va, j + 2 * nw);
+                __builtin_amdgcn_sched_barrier(0);
+                compute.template operator()<false>(kb2, vb2, j + nw);
+                j += 2 * nw;
             }
-            if (j + kWaves < nfull) {
-                issue.template operator()<false>(kb2, vb2, j + kWaves);
+            if (j + nw < nfull) {
+                issue.template operator()<false>(kb2, vb2, j + nw);
+                __builtin_amdgcn_sched_barrier(0);
                 compute.template operator()<false>(ka, va, j);
-                compute.template operator()<false>(kb2, vb2, j + kWaves);
+                compute.template operator()<false>(kb2, vb2, j + nw);
             } else {
                 compute.template operator()<false>(ka, va, j);
             }
         }
         // The partly filled last step goes to the wave whose turn it is.
-        if (tail && wave == nfull % kWaves) {
+        if (tail && wave == nfull % nw) {
             issue.template operator()<true>(ka, va, nfull);
             compute.template operator()<true>(ka, va, nfull);
         }
@@ -454,14 +496,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     // A sequence that fits one partition is finished here; the merge kernel
     // skips it.
     const bool direct = a.PS == 0 || n <= a.PS;
-    for (int i = tid; i < G * D; i += kThreads) {
+    for (int i = tid; i < G * D; i += nthr) {
         const int g = i / D, d = i % D;
         float M = kNegBig;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red[(w * G + g) * (D + 2) + D]);
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, red[(w * G + g) * (D + 2) + D]);
         float L = 0.0f, A = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < nw; ++w) {
             const float *r = red + (w * G + g) * (D + 2);
             const float cw = fexp2(r[D] - M);
             L = fmaf(r[D + 1], cw, L);
@@ -481,31 +523,407 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- grouped-query decode on MFMA
+
+// For 16-bit K/V with G >= 2 query heads per kv head the scores of a 16-token
+// step form a [16 tokens x G heads] tile, so both products run on the matrix
+// cores (the VALU form spends ~700 instructions per step at G = 6):
+//   S^T = K Q^T   v_mfma_f32_16x16x32: A = K (row = token, 8 dims per lane),
+//                 B = Q^T (column = head, heads >= G are zero);
+//   O^T += V^T P^T  v_mfma_f32_16x16x16: B = P^T is the S^T result in place
+//                 (lane l holds tokens 4*(l/16)..+3 of head l%16), A = V^T is
+//                 read transposed from a per-wave LDS tile of the step's V.
+// Lane layouts (A[l%16][k-block l/16], B[k-block l/16][l%16],
+// C[4*(l/16)+j][l%16]) were checked against a host product on gfx950.
+// The per-head running max is shared by the 16 tokens of a step (two lane
+// exchanges), so P can feed one product.  The weights enter the product in
+// the input type: fp16 once (11-bit significand), bf16 as a high part plus
+// the bf16 rounding of the remainder, two products that together carry ~16
+// significant bits (one bf16 rounding alone, 2^-9 per weight, can exceed the
+// output tolerance for short sequences).  The running sum uses the fp32
+// weights.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t vec2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<_Float16> {
+    static constexpr bool kSplit = false;
+    __device__ static float4_t qk(vec4 a, vec4 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    }
+    __device__ static float4_t pv(vec2 a, vec2 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                     __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+    }
+    __device__ static vec2 pack(float x0, float x1, float x2, float x3) {
+        half4_t h = {(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
+        return __builtin_bit_cast(vec2, h);
+    }
+    __device__ static vec2 rest(float, float, float, float, vec2) { return vec2{0u, 0u}; }
+};
+
+template <>
+struct Mma<__bf16> {
+    static constexpr bool kSplit = true;
+    __device__ static float4_t qk(vec4 a, vec4 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a),
+                                                       __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
+    }
+    __device__ static float4_t pv(vec2 a, vec2 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                         __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+    }
+    __device__ static vec2 pack(float x0, float x1, float x2, float x3) {
+        typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
+        bf164_t h = {(__bf16)x0, (__bf16)x1, (__bf16)x2, (__bf16)x3};
+        return __builtin_bit_cast(vec2, h);
+    }
+    // bf16 of x - hi for each weight, hi the packed high parts
+    __device__ static vec2 rest(float x0, float x1, float x2, float x3, vec2 hi) {
+        const float h0 = __uint_as_float(hi.x << 16), h1 = __uint_as_float(hi.x & 0xFFFF0000u);
+        const float h2 = __uint_as_float(hi.y << 16), h3 = __uint_as_float(hi.y & 0xFFFF0000u);
+        return pack(x0 - h0, x1 - h1, x2 - h2, x3 - h3);
+    }
+};
+
+template <typename T, int D, int G, int MODE>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a) {
+    using E = Elem<T>;
+    using M = Mma<T>;
+    static_assert(sizeof(T) == 2 && G >= 2 && G <= 16 && D % 32 == 0, "16-bit grouped-query tile");
+    constexpr int KL = D / 32;            // 16-byte loads per step for K (and for V)
+    constexpr int DS = D / 16;            // 16-wide slices of the output rows
+    constexpr int VROW = D * 2 + 16;      // padded LDS row of a V tile (bytes)
+    constexpr int VTILE = 16 * VROW;      // one step's V tile
+    constexpr int TAB_BYTES = kTableChunk * 4;
+
+    // Dynamic LDS (sized by the launcher): block-table chunk + one V tile per
+    // wave during the loop, then the cross-wave merge buffer.
+    extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
+    char *smem = dyn_smem;
+    __shared__ int32_t s_len[kRankMaxSeqs];
+    __shared__ int32_t s_pick;
+    int32_t *s_tab = reinterpret_cast<int32_t *>(smem);
+
+    const int nthr = blockDim.x;   // 64 * waves
+    const int nw = nthr >> 6;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tok = lane & 15;   // token of the step this lane loads; head of its score column
+    const int kb = lane >> 4;    // k-block: 8 dims of each 32-dim slice; 4 tokens of the score tile
+    const int h = blockIdx.x % a.Hkv;
+    const int part = blockIdx.y;
+    char *vtile = smem + TAB_BYTES + wave * VTILE;
+
+    int s, n;
+    bool staged;
+    pick_work<MODE>(a, s_len, &s_pick, s_tab, tid, nthr, s, n, staged);
+    const int tb = a.PS ? part * a.PS : 0;
+    const int te = a.PS ? min(n, tb + a.PS) : n;
+    const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;
+
+    // B operand of S^T = K Q^T: head tok (zero for tok >= G), dims 32 i + 8 kb ...
+    vec4 qb[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+        qb[i] = tok < G ? load_cached(a.q + ((qrow0 + tok) * D + 32 * i + 8 * kb) * 2)
+                        : vec4{0u, 0u, 0u, 0u};
+
+    if (tb >= te) {
+        if (part == 0)
+            for (int i = tid; i < G * D; i += nthr) E::store(a.out, qrow0 * D + i, 0.0f);
+        return;
+    }
+
+    float m = kNegBig, lsum = 0.0f;
+    float4_t acc[DS];
+#pragma unroll
+    for (int d = 0; d < DS; ++d) acc[d] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    const uint32_t tok_bytes = (uint32_t)a.tok_bytes;
+    uint32_t coff[KL];  // byte offset of this lane's 16 bytes inside a token row
+#pragma unroll
+    for (int i = 0; i < KL; ++i) coff[i] = (uint32_t)((32 * i + 8 * kb) * 2);
+    const int B = 1 << a.log2B;
+    const int32_t *trow = MODE == kDense ? nullptr : a.tables + (int64_t)s * a.MBS;
+    const int64_t head0 = (int64_t)h * a.head_bytes + (MODE == kDense ? (int64_t)s * a.seq_bytes : 0);
+    const char *kh = a.k + head0;
+    const char *vh = a.v + head0;
+
+    const int nblk = (te - tb + B - 1) >> a.log2B;
+    const int chunk_blocks = MODE == kDense ? nblk : kTableChunk;
+
+    for (int cb = 0; cb < nblk; cb += chunk_blocks) {
+        const int cn = min(chunk_blocks, nblk - cb);
+        const int ctb = tb + cb * B;
+        const int cte = min(te, ctb + cn * B);
+        if constexpr (MODE != kDense) {
+            __syncthreads();  // the previous chunk's readers are done / the first chunk is out
+            if (!(cb == 0 && staged)) {
+                stage_table(trow, (tb >> a.log2B) + cb, cn, a.NB, s_tab, tid, nthr);
+                __syncthreads();
+            }
+        }
+        const int nfull = (cte - ctb) / kStepTokens;
+        const int tail = (cte - ctb) % kStepTokens;
+
+        // K and V of step j: lane loads token tok (clamped when MASKED).
+        auto issue = [&]<bool MASKED>(vec4 (&kb_)[KL], vec4 (&vb_)[KL], int j) {
+            const int t0 = ctb + j * kStepTokens;
+            int r = tok;
+            if (MASKED) r = min(r, cte - 1 - t0);
+            int64_t row;
+            if constexpr (MODE == kDense) {
+                row = (int64_t)(t0 + r) * a.tok_bytes;
+            } else if constexpr (MODE == kPagedWide) {
+                const int phys = __builtin_amdgcn_readfirstlane(s_tab[(t0 - ctb) >> a.log2B]);
+                row = (int64_t)phys * a.blk_bytes + (int64_t)((t0 & (B - 1)) + r) * a.tok_bytes;
+            } else {
+                const int t = t0 + r;
+                row = (int64_t)s_tab[(t - ctb) >> a.log2B] * a.blk_bytes +
+                      (int64_t)(t & (B - 1)) * a.tok_bytes;
+            }
+#pragma unroll
+            for (int i = 0; i < KL; ++i) {
+                kb_[i] = load_stream(kh + row + coff[i]);
+                vb_[i] = load_stream(vh + row + coff[i]);
+            }
+        };
+        auto compute = [&]<bool MASKED>(const vec4 (&kb_)[KL], const vec4 (&vb_)[KL], int j) {
+            // the step's V rows into this wave's tile; LDS operations of a wave
+            // run in order, so the previous step's reads have completed
+            char *vt = vtile;
+#pragma unroll
+            for (int i = 0; i < KL; ++i)
+                *reinterpret_cast<vec4 *>(vt + tok * VROW + coff[i]) = vb_[i];
+            // S^T[token 4 kb + jj][head tok]
+            float4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < KL; ++i) sc = M::qk(kb_[i], qb[i], sc);
+            float x[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                x[jj] = sc[jj] * a.qk_scale;
+                if (MASKED && ctb + j * kStepTokens + 4 * kb + jj >= cte) x[jj] = -__builtin_inff();
+            }
+            float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m, mx);
+            const float alpha = fexp2(m - mn);
+            float p[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[jj] - mn);
+            lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            m = mn;
+            const vec2 pb = M::pack(p[0], p[1], p[2], p[3]);
+            const vec2 pr = M::rest(p[0], p[1], p[2], p[3], pb);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int d = 0; d < DS; ++d) {
+                // A operand of O^T += V^T P^T: V[token 4 kb + jj][dim 16 d + tok]
+                const char *src = vt + (4 * kb) * VROW + (16 * d + tok) * 2;
+                const uint32_t v0 = *reinterpret_cast<const uint16_t *>(src);
+                const uint32_t v1 = *reinterpret_cast<const uint16_t *>(src + VROW);
+                const uint32_t v2 = *reinterpret_cast<const uint16_t *>(src + 2 * VROW);
+                const uint32_t v3 = *reinterpret_cast<const uint16_t *>(src + 3 * VROW);
+                const vec2 va = {v0 | (v1 << 16), v2 | (v3 << 16)};
+                acc[d] = acc[d] * alpha;
+                acc[d] = M::pv(va, pb, acc[d]);
+                if constexpr (M::kSplit) acc[d] = M::pv(va, pr, acc[d]);
+            }
+        };
+
+        vec4 ka[KL], va[KL], kc[KL], vc[KL];
+        int j = wave;
+        if (j < nfull) {
+            issue.template operator()<false>(ka, va, j);
+            while (j + 2 * nw < nfull) {
+                issue.template operator()<false>(kc, vc, j + nw);
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+                compute.template operator()<false>(ka, va, j);
+                issue.template operator()<false>(ka, va, j + 2 * nw);
+                __builtin_amdgcn_sched_barrier(0);
+                compute.template operator()<false>(kc, vc, j + nw);
+                j += 2 * nw;
+            }
+            if (j + nw < nfull) {
+                issue.template operator()<false>(kc, vc, j + nw);
+                __builtin_amdgcn_sched_barrier(0);
+                compute.template operator()<false>(ka, va, j);
+                compute.template operator()<false>(kc, vc, j + nw);
+            } else {
+                compute.template operator()<false>(ka, va, j);
+            }
+        }
+        if (tail && wave == nfull % nw) {
+            issue.template operator()<true>(ka, va, nfull);
+            compute.template operator()<true>(ka, va, nfull);
+        }
+    }
+
+    // The four lanes of a head (tok, tok + 16, tok + 32, tok + 48) hold the
+    // same max and partial sums over their tokens.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+
+    __syncthreads();  // table and V tiles are dead; reuse the LDS
+    float *red = reinterpret_cast<float *>(smem);
+    if (tok < G) {
+        float *r = red + (wave * G + tok) * (D + 2);
+#pragma unroll
+        for (int d = 0; d < DS; ++d)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) r[16 * d + 4 * kb + jj] = acc[d][jj];
+        if (kb == 0) {
+            r[D] = m;
+            r[D + 1] = lsum;
+        }
+    }
+    __syncthreads();
+    const bool direct = a.PS == 0 || n <= a.PS;
+    for (int i = tid; i < G * D; i += nthr) {
+        const int g = i / D, d = i % D;
+        float Mx = kNegBig;
+#pragma unroll
+        for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, red[(w * G + g) * (D + 2) + D]);
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < nw; ++w) {
+            const float *r = red + (w * G + g) * (D + 2);
+            const float cw = fexp2(r[D] - Mx);
+            L = fmaf(r[D + 1], cw, L);
+            A = fmaf(r[d], cw, A);
+        }
+        const int64_t qh = qrow0 + g;
+        if (direct) {
+            E::store(a.out, qh * D + d, A / L);
+        } else {
+            const int64_t pi = qh * a.P + part;
+            a.ws_acc[pi * D + d] = A;
+            if (d == 0) {
+                a.ws_ml[pi * 2] = Mx;
+                a.ws_ml[pi * 2 + 1] = L;
+            }
+        }
+    }
+}
+
 // Combines the partitions of one (sequence, query head): with M the largest
 // partition max, out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M).
 // Sequences that fit one partition were written by the decode kernel.
+// 256 threads: thread t owns the 4-float chunk c = t % (D/4) of the row and
+// partitions pg, pg + NG, ... (pg = t / (D/4)).  Up to NG * kMergeRegs
+// partitions every thread issues all its loads before using any, so the
+// kernel waits for memory once; the groups are summed in a fixed order
+// through LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeRegs = 8;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float *ws_acc, const float *ws_ml,
-                                                  const int32_t *lens, void *out, int32_t Hq,
-                                                  int32_t P, int32_t PS, int32_t max_ctx) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(
+    const float *ws_acc, const float *ws_ml, const int32_t *lens, void *out, int32_t Hq, int32_t P,
+    int32_t PS, int32_t max_ctx) {
+    constexpr int C4 = D / 4;                // float4 chunks per row
+    constexpr int NG = kMergeThreads / C4;   // partition groups
+    __shared__ float s_red[kMergeThreads / 64];
+    __shared__ float4 s_acc[NG][C4];
+    __shared__ float s_l[NG];
     const int qh = blockIdx.x;  // s * Hq + h
     const int s = qh / Hq;
-    const int d = threadIdx.x;
-    int n = lens[s];
-    n = n < 0 ? 0 : (n > max_ctx ? max_ctx : n);
+    const int t = threadIdx.x;
+    const int n = clamp_len(lens[s], max_ctx);
     const int np = (n + PS - 1) / PS;
     if (np <= 1) return;
     const float *ml = ws_ml + (int64_t)qh * P * 2;
-    const float *ac = ws_acc + (int64_t)qh * P * D;
-    float M = kNegBig;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.0f, A = 0.0f;
-    for (int p = 0; p < np; ++p) {
-        const float cw = fexp2(ml[2 * p] - M);
-        L = fmaf(ml[2 * p + 1], cw, L);
-        A = fmaf(ac[(int64_t)p * D + d], cw, A);
+    const float4 *ac = reinterpret_cast<const float4 *>(ws_acc + (int64_t)qh * P * D);
+    const int c = t % C4, pg = t / C4;
+
+    auto block_max = [&](float x) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+        if ((t & 63) == 0) s_red[t >> 6] = x;
+        __syncthreads();
+        float M = s_red[0];
+#pragma unroll
+        for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w]);
+        return M;
+    };
+
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lsum = 0.0f;
+    if (np <= NG * kMergeRegs) {
+        float mp[kMergeRegs], lp[kMergeRegs];
+        float4 x[kMergeRegs];
+#pragma unroll
+        for (int k = 0; k < kMergeRegs; ++k) {
+            const int p = pg + k * NG;
+            const bool ok = p < np;
+            const int pc = ok ? p : np - 1;  // every load stays inside this row's partials
+            const float m0 = ml[2 * pc], l0 = ml[2 * pc + 1];
+            const float4 x0 = ac[(int64_t)pc * C4 + c];
+            mp[k] = ok ? m0 : kNegBig;
+            lp[k] = ok ? l0 : 0.0f;
+            x[k] = ok ? x0 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        float mx = kNegBig;
+#pragma unroll
+        for (int k = 0; k < kMergeRegs; ++k) mx = fmaxf(mx, mp[k]);
+        const float M = block_max(mx);
+#pragma unroll
+        for (int k = 0; k < kMergeRegs; ++k) {
+            const float w = fexp2(mp[k] - M);  // 0 for the padding entries
+            a.x = fmaf(x[k].x, w, a.x);
+            a.y = fmaf(x[k].y, w, a.y);
+            a.z = fmaf(x[k].z, w, a.z);
+            a.w = fmaf(x[k].w, w, a.w);
+            lsum = fmaf(lp[k], w, lsum);
+        }
+    } else {
+        float mx = kNegBig;
+        for (int p = t; p < np; p += kMergeThreads) mx = fmaxf(mx, ml[2 * p]);
+        const float M = block_max(mx);
+#pragma unroll 4
+        for (int p = pg; p < np; p += NG) {
+            const float w = fexp2(ml[2 * p] - M);
+            const float4 x = ac[(int64_t)p * C4 + c];
+            a.x = fmaf(x.x, w, a.x);
+            a.y = fmaf(x.y, w, a.y);
+            a.z = fmaf(x.z, w, a.z);
+            a.w = fmaf(x.w, w, a.w);
+            lsum = fmaf(ml[2 * p + 1], w, lsum);
+        }
     }
-    Elem<T>::store(out, (int64_t)qh * D + d, A / L);
+    s_acc[pg][c] = a;
+    if (c == 0) s_l[pg] = lsum;
+    __syncthreads();
+    if (t < C4) {
+        float4 r = s_acc[0][t];
+        float L = s_l[0];
+#pragma unroll
+        for (int g = 1; g < NG; ++g) {
+            const float4 x = s_acc[g][t];
+            r.x += x.x;
+            r.y += x.y;
+            r.z += x.z;
+            r.w += x.w;
+            L += s_l[g];
+        }
+        const int64_t o = (int64_t)qh * D + 4 * t;
+        Elem<T>::store(out, o + 0, r.x / L);
+        Elem<T>::store(out, o + 1, r.y / L);
+        Elem<T>::store(out, o + 2, r.z / L);
+        Elem<T>::store(out, o + 3, r.w / L);
+    }
 }
 
 template <typename T, int D, int G>
@@ -533,7 +951,13 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.max_ctx = l.max_ctx;
     a.PS = l.PS;
     a.P = l.P;
-    a.rank = (l.S > 1 && l.S <= kRankMaxSeqs) ? 1 : 0;
+    // Ranking costs the workgroup one dependent round trip; it pays only when
+    // the grid is too large to be resident at once, so that order matters.
+    a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512) ? 1 : 0;
+    {
+        const int64_t span = l.PS ? (l.PS < l.max_ctx ? l.PS : l.max_ctx) : l.max_ctx;
+        a.spec_blocks = (int32_t)((span + B - 1) / B);
+    }
     const int64_t row = (int64_t)D * sizeof(T);        // one head's row
     const int64_t span = l.dense ? l.pos_stride : B;   // tokens per block / per sequence
     if (l.layout == 0) {  // token-major: [..., tokens, Hkv, D]
@@ -546,15 +970,36 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.blk_bytes = l.dense ? 0 : row * l.Hkv * B;
     a.seq_bytes = l.dense ? row * l.Hkv * l.pos_stride : 0;
     dim3 grid((unsigned)((int64_t)l.S * l.Hkv), (unsigned)l.P, 1);
-    if (l.dense)
-        hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), grid, dim3(kThreads), 0, st, a);
-    else if (l.B >= kStepTokens)
-        hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedWide>), grid, dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedNarrow>), grid, dim3(kThreads), 0, st, a);
+    // 8 waves per workgroup when the grid is small (fewer than four
+    // workgroups per CU): each wave then walks half as many steps, which
+    // doubles the loads in flight; 4 waves otherwise.
+    const int64_t wgs = (int64_t)l.S * l.Hkv * l.P;
+    const int nw = (wgs < 1024 && max_waves<T>() >= 8) ? 8 : 4;
+    const dim3 block(64 * nw);
+    const size_t red_bytes = (size_t)nw * G * (D + 2) * 4;
+    if constexpr (sizeof(T) == 2 && G >= 2) {  // grouped-query heads: matrix cores
+        const size_t loop_bytes = (size_t)kTableChunk * 4 + (size_t)nw * 16 * (2 * D + 16);
+        const size_t lds = loop_bytes > red_bytes ? loop_bytes : red_bytes;
+        if (l.dense)
+            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kDense>), grid, block, lds, st, a);
+        else if (l.B >= kStepTokens)
+            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kPagedWide>), grid, block, lds, st, a);
+        else
+            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kPagedNarrow>), grid, block, lds, st, a);
+    } else {
+        const size_t loop_bytes = (size_t)kTableChunk * 4;
+        const size_t lds = loop_bytes > red_bytes ? loop_bytes : red_bytes;
+        if (l.dense)
+            hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), grid, block, lds, st, a);
+        else if (l.B >= kStepTokens)
+            hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedWide>), grid, block, lds, st, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedNarrow>), grid, block, lds, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || l.PS == 0) return e;
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)l.S * l.Hq)), dim3(D), 0, st,
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)l.S * l.Hq)),
+                       dim3(kMergeThreads), 0, st,
                        a.ws_acc, a.ws_ml, l.lens, l.out, l.Hq, l.P, l.PS, l.max_ctx);
     return hipGetLastError();
 }
