@@ -75,7 +75,11 @@ typedef enum {
                                 65535 partitions or 2^31 - 1 (seq, head) rows,
                                 a token row (all kv heads) above 128 MiB      */
     PA_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small       */
-    PA_ERR_HIP = -7          /* the HIP launch failed                         */
+    PA_ERR_HIP = -7,         /* the HIP launch failed                         */
+    PA_ERR_NO_BLOCKS = -8,   /* block manager: the pool cannot supply the
+                                blocks a call needs (nothing was changed)    */
+    PA_ERR_STATE = -9        /* block manager: a sequence handle is not live,
+                                repeated, or on the wrong side for the call  */
 } pa_status;
 
 /* Shape of one decode call (host struct). */
@@ -201,6 +205,11 @@ const char *pa_status_string(int status);
 
 /* Static text naming the build: target, kernel variants, compiler. */
 const char *pa_build_info(void);
+
+/* Name of the HIP error (e.g. "hipErrorInvalidValue") behind the calling
+ * thread's most recent PA_ERR_HIP, or "" if this thread has had none.  The
+ * string is static; it stays valid for the life of the process. */
+const char *pa_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ is not built, every call raises.
 Entry points (same names as the C ABI):
   pa_decode, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
   pa_copy_blocks
+and the host block manager (``include/pa_block_manager.h``) as the class
+``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
 """
 from __future__ import annotations
 
@@ -22,13 +24,16 @@ __all__ = ["pa_decode", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_ALIGN", -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_WORKSPACE",
-          -7: "PA_ERR_HIP"}
+          -7: "PA_ERR_HIP", -8: "PA_ERR_NO_BLOCKS", -9: "PA_ERR_STATE"}
 
 
 class PaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
+        self.name = STATUS.get(status, str(status))
         msg = lib().pa_status_string(status).decode()
+        if status == -7:
+            msg += f" ({lib().pa_last_hip_error().decode()})"
         super().__init__(f"{what}: {msg}")
 
 
@@ -65,6 +70,13 @@ def lib():
     """The loaded HIP library; raises if it has not been built."""
     global _lib
     if _lib is None:
+        # torch brings its own HIP runtime (soname libamdhip64.so.7).  Load it
+        # before libpa.so so that the loader binds libpa's dependency to that
+        # same copy: tensors, streams and these kernels must share one
+        # runtime.  Loaded the other way round, the process would hold two
+        # HIP runtimes and this library's launches would not see the device.
+        import torch  # noqa: F401
+
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"HIP library {LIB_PATH} is not built; run `python -m paged_kv_cache_pa_amd.build` "
@@ -84,6 +96,11 @@ def lib():
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_build_info.argtypes = []
         L.pa_build_info.restype = ctypes.c_char_p
+        L.pa_last_hip_error.argtypes = []
+        L.pa_last_hip_error.restype = ctypes.c_char_p
+        from .block_manager import declare as _declare_bm
+
+        _declare_bm(L)
         _lib = L
     return _lib
 

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_kernels.hip", "pa_abi.cpp"]
+SOURCES = ["pa_kernels.hip", "pa_abi.cpp", "block_manager.cpp"]
 ARCH = "gfx950"
 
 

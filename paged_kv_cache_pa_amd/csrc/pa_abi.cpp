@@ -10,6 +10,15 @@
 
 namespace {
 
+// HIP error code behind the calling thread's most recent PA_ERR_HIP.
+thread_local int last_hip_error = 0;
+
+int hip_status(int e) {
+    if (e == 0) return PA_OK;
+    last_hip_error = e;
+    return PA_ERR_HIP;
+}
+
 int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
 
 bool dtype_ok(int32_t dtype) { return dtype == PA_F32 || dtype == PA_F16 || dtype == PA_BF16; }
@@ -105,7 +114,7 @@ int run_decode(const void *q, const void *k, const void *v, const int32_t *table
     l.layout = p->layout;
     l.dense = dense;
     const int e = pa::launch_decode(l, stream);
-    return e ? PA_ERR_HIP : PA_OK;
+    return hip_status(e);
 }
 
 int check_cache_params(const pa_cache_params *p) {
@@ -168,7 +177,7 @@ int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_
     const int e = pa::launch_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, num_tokens,
                                          p->num_blocks, p->block_size, p->num_kv_heads, row,
                                          p->layout, stream);
-    return e ? PA_ERR_HIP : PA_OK;
+    return hip_status(e);
 }
 
 int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int32_t num_pairs,
@@ -184,7 +193,7 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
                         elem_bytes(p->dtype);
     const int e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, p->num_blocks,
                                          blk, stream);
-    return e ? PA_ERR_HIP : PA_OK;
+    return hip_status(e);
 }
 
 const char *pa_status_string(int status) {
@@ -197,10 +206,16 @@ const char *pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: head_dim or head grouping not built";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: split-K workspace missing or too small";
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP launch failed";
+        case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the block pool cannot supply the call";
+        case PA_ERR_STATE: return "PA_ERR_STATE: sequence handle not live, repeated or on the wrong side";
     }
     return "unknown pa_status";
 }
 
 const char *pa_build_info(void) { return pa::kernel_build_info(); }
+
+const char *pa_last_hip_error(void) {
+    return last_hip_error ? pa::hip_error_name(last_hip_error) : "";
+}
 
 }  // extern "C"

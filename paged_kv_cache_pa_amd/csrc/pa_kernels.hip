@@ -50,6 +50,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "pa_launch.h"
 
 namespace pa {
@@ -926,6 +928,51 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     }
 }
 
+// Workgroups of one kernel that a CU holds at once, at a given block size and
+// dynamic LDS, times the CU count of the current device.  Queried once per
+// (kernel, waves, device) and cached; the query itself is host-only.
+struct ResidentKey {
+    const void *fn;
+    int nw, dev;
+    size_t lds;
+};
+
+static int64_t resident_workgroups(const void *fn, int nw, size_t lds) {
+    static std::mutex mu;
+    static ResidentKey keys[64];
+    static int64_t vals[64];
+    static int n = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < n; ++i)
+        if (keys[i].fn == fn && keys[i].nw == nw && keys[i].dev == dev && keys[i].lds == lds)
+            return vals[i];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * nw, lds) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int64_t r = (int64_t)per_cu * cus;
+    if (n < 64) {
+        keys[n] = ResidentKey{fn, nw, dev, lds};
+        vals[n++] = r;
+    }
+    return r;
+}
+
+// Waves per workgroup.  8 waves halve the steps each wave walks and double
+// the loads a workgroup keeps in flight, which pays when the grid is small,
+// but only while every workgroup is still resident at once: a grid that
+// spills into a second round of workgroups finishes in two round trips of
+// the longest workgroup.  So: 8 waves when the whole grid fits at 8; else 4
+// when it fits at 4; else (a grid several times the machine) 4.
+static int pick_waves(const void *fn8, const void *fn4, int64_t wgs, size_t lds8, size_t lds4) {
+    if (fn8 == nullptr) return 4;
+    if (wgs <= resident_workgroups(fn8, 8, lds8)) return 8;
+    if (wgs <= resident_workgroups(fn4, 4, lds4)) return 4;
+    return wgs < 1024 ? 8 : 4;
+}
+
 template <typename T, int D, int G>
 static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     DecodeArgs a;
@@ -970,32 +1017,33 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.blk_bytes = l.dense ? 0 : row * l.Hkv * B;
     a.seq_bytes = l.dense ? row * l.Hkv * l.pos_stride : 0;
     dim3 grid((unsigned)((int64_t)l.S * l.Hkv), (unsigned)l.P, 1);
-    // 8 waves per workgroup when the grid is small (fewer than four
-    // workgroups per CU): each wave then walks half as many steps, which
-    // doubles the loads in flight; 4 waves otherwise.
     const int64_t wgs = (int64_t)l.S * l.Hkv * l.P;
-    const int nw = (wgs < 1024 && max_waves<T>() >= 8) ? 8 : 4;
-    const dim3 block(64 * nw);
-    const size_t red_bytes = (size_t)nw * G * (D + 2) * 4;
+    auto red_bytes = [](int nw) { return (size_t)nw * G * (D + 2) * 4; };
+    auto max2 = [](size_t x, size_t y) { return x > y ? x : y; };
+    using Kern = void (*)(DecodeArgs);
+    Kern fn;
+    int nw;
+    size_t lds;
     if constexpr (sizeof(T) == 2 && G >= 2) {  // grouped-query heads: matrix cores
-        const size_t loop_bytes = (size_t)kTableChunk * 4 + (size_t)nw * 16 * (2 * D + 16);
-        const size_t lds = loop_bytes > red_bytes ? loop_bytes : red_bytes;
-        if (l.dense)
-            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kDense>), grid, block, lds, st, a);
-        else if (l.B >= kStepTokens)
-            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kPagedWide>), grid, block, lds, st, a);
-        else
-            hipLaunchKernelGGL((decode_mma_kernel<T, D, G, kPagedNarrow>), grid, block, lds, st, a);
+        auto lds_of = [&](int w) {
+            return max2((size_t)kTableChunk * 4 + (size_t)w * 16 * (2 * D + 16), red_bytes(w));
+        };
+        fn = l.dense ? decode_mma_kernel<T, D, G, kDense>
+           : l.B >= kStepTokens ? decode_mma_kernel<T, D, G, kPagedWide>
+                                : decode_mma_kernel<T, D, G, kPagedNarrow>;
+        nw = pick_waves((const void *)fn, (const void *)fn, wgs, lds_of(8), lds_of(4));
+        lds = lds_of(nw);
     } else {
-        const size_t loop_bytes = (size_t)kTableChunk * 4;
-        const size_t lds = loop_bytes > red_bytes ? loop_bytes : red_bytes;
-        if (l.dense)
-            hipLaunchKernelGGL((decode_kernel<T, D, G, kDense>), grid, block, lds, st, a);
-        else if (l.B >= kStepTokens)
-            hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedWide>), grid, block, lds, st, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<T, D, G, kPagedNarrow>), grid, block, lds, st, a);
+        auto lds_of = [&](int w) { return max2((size_t)kTableChunk * 4, red_bytes(w)); };
+        fn = l.dense ? decode_kernel<T, D, G, kDense>
+           : l.B >= kStepTokens ? decode_kernel<T, D, G, kPagedWide>
+                                : decode_kernel<T, D, G, kPagedNarrow>;
+        nw = pick_waves(max_waves<T>() >= 8 ? (const void *)fn : nullptr, (const void *)fn, wgs,
+                        lds_of(8), lds_of(4));
+        lds = lds_of(nw);
     }
+    (void)hipGetLastError();  // an error left by other code is not this launch's
+    hipLaunchKernelGGL(fn, grid, dim3(64 * nw), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || l.PS == 0) return e;
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)l.S * l.Hq)),
@@ -1079,6 +1127,7 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
     int64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
+    (void)hipGetLastError();  // an error left by other code is not this launch's
     hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, (const vec4 *)k_new, (const vec4 *)v_new,
                        (char *)k_cache, (char *)v_cache, slots, total, rv, hkv, log2B,
@@ -1115,6 +1164,7 @@ int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32
     int64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
+    (void)hipGetLastError();  // an error left by other code is not this launch's
     hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, (vec4 *)k_cache, (vec4 *)v_cache, pairs, total, bv,
                        num_blocks);

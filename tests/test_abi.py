@@ -35,7 +35,9 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"pa_decode", "pa_decode_dense", "pa_cache_write", "pa_copy_blocks",
-            "pa_decode_workspace_size", "pa_status_string", "pa_build_info"} <= set(names)
+            "pa_decode_workspace_size", "pa_status_string", "pa_build_info",
+            "pa_bm_create", "pa_bm_destroy", "pa_bm_reserve", "pa_bm_tables", "pa_bm_fork",
+            "pa_bm_free", "pa_bm_swap_out", "pa_bm_swap_in"} <= set(names)
     for n in names:
         assert hasattr(L, n), f"{n} declared in include/ but not exported"
 
@@ -206,3 +208,18 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         pa.lib()
     importlib.reload(pa)
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library before anything imports torch must still leave the
+    process with one HIP runtime (torch's), not torch's and the system's."""
+    import subprocess
+    import sys
+
+    code = ("import paged_kv_cache_pa_amd as pa; pa.lib(); import torch; "
+            "m = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in m if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1"
