@@ -187,6 +187,141 @@ def copy_blocks_rate(rounds=15):
             "replicas": R}
 
 
+def copy_layers_rate(rounds=10, layers=40):
+    """pa_copy_blocks_layers: the 80 copy-on-write pairs of the
+    parallel-sampling workload applied to every one of OPT-13B's 40 layers in
+    one launch.  The pairs' blocks are renumbered into a compact pool per layer
+    (2 x 160 blocks x 160 KiB x 40 layers = 2 GiB, past the last-level cache)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+    import workloads as W
+
+    pairs = W.config4(poison=False).paged.block_pairs
+    ids, inv = np.unique(pairs, return_inverse=True)
+    compact = inv.reshape(pairs.shape).astype(np.int32)
+    nb, B, H, D = len(ids), 16, 40, 128
+    ks = [torch.empty((nb, H, B, D), dtype=torch.float16, device="cuda") for _ in range(layers)]
+    vs = [torch.empty_like(k) for k in ks]
+    for t in ks + vs:
+        t.normal_()
+    bp = torch.from_numpy(compact).cuda()
+    st = torch.cuda.current_stream()
+
+    def f(i):
+        pa.pa_copy_blocks_layers(ks, vs, bp, layout="HND")
+
+    f(0)
+    t = float(np.median([time_group(f, 1, st) for _ in range(rounds)]))
+    n = compact.shape[0]
+    nbytes = 2 * 2 * n * layers * B * H * D * 2 + 8 * n
+    del ks, vs
+    torch.cuda.empty_cache()
+    return {"pairs": int(n), "layers": layers, "us": round(t * 1e6, 1),
+            "GB_s": round(nbytes / t / 1e9, 1), "launches": -(-layers // 64)}
+
+
+def swap_rate(rounds=5, mib=64):
+    """Swapping between HBM and pinned host memory at block sizes 16 / 64 /
+    256 tokens (OPT-13B layer geometry, 40 heads x 128 dims fp16): one
+    pa_swap_blocks launch for all blocks, against one asynchronous copy per
+    K / V block (torch copy_, a hipMemcpyAsync each) for the same blocks.
+    ``mib`` MiB of K+V move each way."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    res = {}
+    rng = np.random.default_rng(7)
+    st = torch.cuda.current_stream()
+    for B in (16, 64, 256):
+        blk = B * 40 * 128 * 2
+        n = max(1, (mib << 20) // (2 * blk))
+        gk = torch.randn((2 * n, 40, B, 128), dtype=torch.float16, device="cuda")
+        gv = torch.randn_like(gk)
+        hk = torch.empty((n, 40, B, 128), dtype=torch.float16, pin_memory=True)
+        hv = torch.empty_like(hk, pin_memory=True)
+        g_ids = rng.permutation(2 * n)[:n]
+        out_pairs = torch.from_numpy(np.stack([g_ids, np.arange(n)], 1).astype(np.int32)).cuda()
+        in_pairs = torch.from_numpy(np.stack([np.arange(n), g_ids], 1).astype(np.int32)).cuda()
+
+        def k_out(i):
+            pa.pa_swap_blocks([hk], [hv], [gk], [gv], out_pairs, layout="HND")
+
+        def k_in(i):
+            pa.pa_swap_blocks([gk], [gv], [hk], [hv], in_pairs, layout="HND")
+
+        def c_out(i):
+            for j, g in enumerate(g_ids):
+                hk[j].copy_(gk[g], non_blocking=True)
+                hv[j].copy_(gv[g], non_blocking=True)
+
+        def c_in(i):
+            for j, g in enumerate(g_ids):
+                gk[g].copy_(hk[j], non_blocking=True)
+                gv[g].copy_(hv[j], non_blocking=True)
+
+        row = {"blocks": int(n), "block_KiB": blk // 1024}
+        nbytes = 2 * n * blk
+        for name, fn in (("kernel_out", k_out), ("kernel_in", k_in), ("per_block_out", c_out),
+                         ("per_block_in", c_in)):
+            fn(0)
+            t = float(np.median([time_group(fn, 1, st) for _ in range(rounds)]))
+            row[name + "_GB_s"] = round(nbytes / t / 1e9, 1)
+        res[f"B{B}"] = row
+        del gk, gv, hk, hv
+        torch.cuda.empty_cache()
+    return res
+
+
+def block_manager_rate(steps=400):
+    """Host cost of the block manager for one decode iteration of the
+    OPT-13B-shape batch: reserve one slot for each of the 64 sequences, then
+    export the block tables and lengths pa_decode reads.  Host-only; median
+    microseconds per iteration, through the Python binding and as the bare
+    C calls on preallocated buffers."""
+    import ctypes
+    import time as _t
+
+    import workloads as W
+    from paged_kv_cache_pa_amd.block_manager import BlockManager
+
+    lens, _ = W.config2_lens()
+    B, mbs = 16, 256
+    nb = int(sum(-(-int(n) // B) for n in lens)) + 64 * (2 * steps // B + 2)
+    bm = BlockManager(nb, 0, B)
+    seqs = [bm.new_seq() for _ in lens]
+    bm.reserve(seqs, [int(n) for n in lens])
+    ones = [1] * len(seqs)
+    py = []
+    for _ in range(steps):
+        t0 = _t.perf_counter()
+        bm.reserve(seqs, ones)
+        bm.tables(seqs, mbs)
+        py.append(_t.perf_counter() - t0)
+    L = bm._L
+    S = len(seqs)
+    s_arr = (ctypes.c_int32 * S)(*seqs)
+    k_arr = (ctypes.c_int32 * S)(*ones)
+    slots = (ctypes.c_int32 * S)()
+    pairs = (ctypes.c_int32 * (2 * S))()
+    tables = (ctypes.c_int32 * (S * mbs))()
+    cl = (ctypes.c_int32 * S)()
+    npairs = ctypes.c_int32()
+    native = []
+    for _ in range(steps):
+        t0 = _t.perf_counter()
+        rc = L.pa_bm_reserve(bm._h, s_arr, k_arr, S, slots, S, pairs, S, ctypes.byref(npairs))
+        rc |= L.pa_bm_tables(bm._h, s_arr, S, tables, mbs, cl)
+        native.append(_t.perf_counter() - t0)
+        if rc:
+            raise RuntimeError(f"block manager call failed: {rc}")
+    bm.close()
+    return {"seqs": S, "binding_us": round(float(np.median(py)) * 1e6, 1),
+            "native_us": round(float(np.median(native)) * 1e6, 2),
+            "what": "median per decode iteration: reserve(64 x 1 token) + tables export"}
+
+
 def _dev_pool(a, layout):
     import torch
 
@@ -383,7 +518,7 @@ def counters_run(args):
 
 
 DECODE_KERNEL_PREFIX = "_ZN2pa13decode_kernelIDF16_Li128ELi1ELi1E"  # fp16, D 128, G 1, paged B>=16
-COPY_KERNEL_PREFIX = "pa::copy_blocks_kernel"
+COPY_KERNEL_PREFIX = "pa::move_blocks_kernel"
 
 
 def _rows(path):
@@ -437,7 +572,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, commands):
         "kernel_sha256_16": meta["kernel_sha256_16"],
         "fetch_kib_per_dispatch": round(f_dec, 3), "write_kib_per_dispatch": round(w_dec, 3),
         "dispatches": [nf, nw],
-        "calibration": {"kernel": "pa::copy_blocks_kernel (plain block copy)",
+        "calibration": {"kernel": "pa::move_blocks_kernel (pa_copy_blocks, a plain block copy)",
                         "read_bytes": meta["copy_read_bytes"], "write_bytes": meta["copy_write_bytes"],
                         "fetch_kib": round(f_cpy, 3), "write_kib": round(w_cpy, 3),
                         "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5)},
@@ -647,6 +782,13 @@ def main():
         except Exception as e:
             result["copy_blocks"] = {"error": repr(e)}
         log("copy_blocks done")
+        for key, fn in (("copy_blocks_layers", copy_layers_rate), ("swap", swap_rate),
+                        ("block_manager", block_manager_rate)):
+            try:
+                result[key] = fn()
+            except Exception as e:
+                result[key] = {"error": repr(e)}
+            log(f"{key} done")
         result["cpu_baseline"] = cpu_baseline(p)
         log("cpu baseline done")
     print(json.dumps(result), flush=True)

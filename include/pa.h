@@ -200,6 +200,43 @@ int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_
 int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs,
                    int32_t num_pairs, const pa_cache_params *p, void *stream);
 
+/*
+ * copy_blocks for every layer of a model at once: one block id names the
+ * same position in every layer's pool ([Res] "A paged KV cache, in code"),
+ * so one list of pairs serves all layers, and the copies of all layers run
+ * in one launch per 64 layers ([Kwon] §3.4 "Kernel-Level Optimizations",
+ * item 3: block copies fused across layers).  Same rules as pa_copy_blocks
+ * per layer.
+ * k_caches, v_caches: HOST arrays of num_layers device pointers, one pool
+ * per layer, all with the geometry ``p``; read during the call only.
+ * block_pairs: device pointer.  PA_ERR_UNSUPPORTED if num_pairs * min(
+ * num_layers, 64) * 512 reaches 2^32 (split the call).
+ */
+int pa_copy_blocks_layers(void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                          const int32_t *block_pairs, int32_t num_pairs,
+                          const pa_cache_params *p, void *stream);
+
+/*
+ * swap_blocks: moves whole blocks between two pools of the same block
+ * geometry, for every layer, in one launch per 64 layers: for each pair
+ * (src, dst), layer l: dst_k[l][dst] = src_k[l][src], dst_v[l][dst] =
+ * src_v[l][src] ([Kwon] §3.4 "Scheduling and Preemption": swapping copies
+ * the evicted blocks to CPU memory and back; the pairs come from the block
+ * manager's pa_bm_swap_out / pa_bm_swap_in).  Either pool may live in device
+ * memory or in pinned host memory that the device can access (e.g.
+ * hipHostMalloc); one kernel reads and writes both, so many small blocks do
+ * not cost one DMA transfer each.  Pairs with src outside [0,
+ * src_num_blocks) or dst outside [0, dst_num_blocks) are skipped.  The two
+ * pools must not overlap; destinations must be distinct.
+ * dst_k, dst_v, src_k, src_v: HOST arrays of num_layers pool pointers.
+ * block_pairs: device-accessible.  p: block geometry (its num_blocks is not
+ * used).
+ */
+int pa_swap_blocks(void *const *dst_k, void *const *dst_v, int32_t dst_num_blocks,
+                   const void *const *src_k, const void *const *src_v, int32_t src_num_blocks,
+                   int32_t num_layers, const int32_t *block_pairs, int32_t num_pairs,
+                   const pa_cache_params *p, void *stream);
+
 /* Static text for a pa_status value (never NULL). */
 const char *pa_status_string(int status);
 

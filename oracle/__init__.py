@@ -178,6 +178,31 @@ def copy_blocks(k_cache, v_cache, block_pairs, dtype, layout="NHD"):
     return kc, vc
 
 
+def copy_blocks_layers(k_caches, v_caches, block_pairs, dtype, layout="NHD"):
+    """copy_blocks applied to every layer's pool ([Kwon] §3.4 "Kernel-Level
+    Optimizations", item 3: the same pairs for all layers).  Returns new
+    lists of pools."""
+    out = [copy_blocks(k, v, block_pairs, dtype, layout) for k, v in zip(k_caches, v_caches)]
+    return [k for k, _ in out], [v for _, v in out]
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs):
+    """Whole blocks from one pool into another, every layer ([Kwon] §3.4
+    "Scheduling and Preemption": swapping copies a group's blocks to the CPU
+    block pool and back).  For each (src, dst) pair in order and each layer:
+    dst[dst_id] = src[src_id], byte for byte; pairs naming a block outside
+    either pool are skipped.  Returns new lists of destination pools."""
+    bp = np.asarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    ok, ov = [np.array(x, copy=True, order="C") for x in dst_k], [np.array(x, copy=True, order="C") for x in dst_v]
+    for layer in range(len(src_k)):
+        nsrc, ndst = src_k[layer].shape[0], ok[layer].shape[0]
+        for s, d in bp:
+            if 0 <= s < nsrc and 0 <= d < ndst:
+                ok[layer][d] = src_k[layer][s]
+                ov[layer][d] = src_v[layer][s]
+    return ok, ov
+
+
 def half_to_double(bits: int) -> float:
     return lib().oracle_half_to_double(int(bits))
 

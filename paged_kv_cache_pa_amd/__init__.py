@@ -8,7 +8,7 @@ is not built, every call raises.
 
 Entry points (same names as the C ABI):
   pa_decode, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
-  pa_copy_blocks
+  pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks
 and the host block manager (``include/pa_block_manager.h``) as the class
 ``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
 """
@@ -20,7 +20,8 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["pa_decode", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
-           "pa_copy_blocks", "PaError", "lib", "LIB_PATH", "STATUS"]
+           "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "PaError", "lib",
+           "LIB_PATH", "STATUS"]
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_ALIGN", -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_WORKSPACE",
@@ -89,8 +90,10 @@ def lib():
         L.pa_decode_dense.argtypes = [P, P, P, P, ctypes.c_float, P, DP, I32, P, SZ, P]
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I32, CP, P]
+        L.pa_copy_blocks_layers.argtypes = [P, P, I32, P, I32, CP, P]
+        L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
         for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_dense", "pa_cache_write",
-                  "pa_copy_blocks"):
+                  "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
@@ -267,3 +270,61 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, *, stream=None, layout="NHD"):
     _check(lib().pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
                                 int(block_pairs.shape[0]), ctypes.byref(p), _stream(stream)),
            "pa_copy_blocks")
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))(*[t.data_ptr() for t in tensors])
+    return arr
+
+
+def _pools(ks, vs, name, allow_host=False):
+    """Per-layer pools: same shape and dtype, device tensors (or pinned host
+    tensors where ``allow_host``)."""
+    if len(ks) == 0 or len(ks) != len(vs):
+        raise ValueError(f"{name}: one K and one V pool per layer, at least one layer")
+    for t in list(ks) + list(vs):
+        if t.shape != ks[0].shape or t.dtype != ks[0].dtype or t.dim() != 4:
+            raise ValueError(f"{name}: every pool must match the first one's shape and dtype")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: pools must be contiguous")
+        if not (t.is_cuda or (allow_host and t.is_pinned())):
+            raise ValueError(f"{name}: pools must be GPU tensors" +
+                             (" or pinned host tensors" if allow_host else ""))
+
+
+def pa_copy_blocks_layers(k_caches, v_caches, block_pairs, *, stream=None, layout="NHD"):
+    """pa_copy_blocks over every layer's pool (lists of [NB, ...] tensors) in
+    one launch per 64 layers."""
+    import torch
+
+    _pools(k_caches, v_caches, "pa_copy_blocks_layers")
+    _need(block_pairs, "block_pairs", 2, torch.int32)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    p = _cache_params(k_caches[0], layout)
+    _check(lib().pa_copy_blocks_layers(_ptr_array(k_caches), _ptr_array(v_caches),
+                                       len(k_caches), _ptr(block_pairs),
+                                       int(block_pairs.shape[0]), ctypes.byref(p),
+                                       _stream(stream)), "pa_copy_blocks_layers")
+
+
+def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None, layout="NHD"):
+    """Move blocks between two pools (lists per layer, GPU or pinned host
+    tensors) for every (src, dst) row of block_pairs [n, 2] (a GPU tensor)."""
+    import torch
+
+    _pools(dst_k, dst_v, "pa_swap_blocks dst", allow_host=True)
+    _pools(src_k, src_v, "pa_swap_blocks src", allow_host=True)
+    if len(dst_k) != len(src_k):
+        raise ValueError("pa_swap_blocks: same number of layers on both sides")
+    _need(block_pairs, "block_pairs", 2, torch.int32)
+    if block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    ps, pd = _cache_params(src_k[0], layout), _cache_params(dst_k[0], layout)
+    if (ps.block_size, ps.num_kv_heads, ps.head_dim, ps.dtype) != \
+            (pd.block_size, pd.num_kv_heads, pd.head_dim, pd.dtype):
+        raise ValueError("pa_swap_blocks: both pools need the same block geometry and dtype")
+    _check(lib().pa_swap_blocks(_ptr_array(dst_k), _ptr_array(dst_v), pd.num_blocks,
+                                _ptr_array(src_k), _ptr_array(src_v), ps.num_blocks,
+                                len(src_k), _ptr(block_pairs), int(block_pairs.shape[0]),
+                                ctypes.byref(ps), _stream(stream)), "pa_swap_blocks")

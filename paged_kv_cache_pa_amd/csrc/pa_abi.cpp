@@ -127,6 +127,48 @@ int check_cache_params(const pa_cache_params *p) {
     return PA_OK;
 }
 
+// Shared by copy_blocks (one layer, one pool), copy_blocks_layers and
+// swap_blocks (two pools): validate, then one launch per kMaxLayers layers.
+int move_blocks(const void *const *src_k, const void *const *src_v, int32_t src_blocks,
+                void *const *dst_k, void *const *dst_v, int32_t dst_blocks, int32_t layers,
+                const int32_t *pairs, int32_t n, const pa_cache_params *p, void *stream) {
+    const int st = check_cache_params(p);
+    if (st != PA_OK) return st;
+    if (n < 0 || layers < 1) return PA_ERR_SHAPE;
+    if (n == 0) return PA_OK;
+    if (!src_k || !src_v || !dst_k || !dst_v || !pairs) return PA_ERR_NULL;
+    for (int32_t l = 0; l < layers; ++l) {
+        if (!src_k[l] || !src_v[l] || !dst_k[l] || !dst_v[l]) return PA_ERR_NULL;
+        if (!aligned16(src_k[l]) || !aligned16(src_v[l]) || !aligned16(dst_k[l]) ||
+            !aligned16(dst_v[l]))
+            return PA_ERR_ALIGN;
+    }
+    if ((uintptr_t)pairs & 3u) return PA_ERR_ALIGN;
+    const int64_t blk = (int64_t)p->block_size * p->num_kv_heads * p->head_dim *
+                        elem_bytes(p->dtype);
+    // grid x = pairs * layers * 2 workgroups of 256 threads; grid y = 16 KiB chunks
+    const int32_t per = layers < pa::kMaxLayers ? layers : pa::kMaxLayers;
+    if ((int64_t)n * per * 2 * 256 >= ((int64_t)1 << 32)) return PA_ERR_UNSUPPORTED;
+    if (blk / 16 > (int64_t)65535 * 256 * 4) return PA_ERR_UNSUPPORTED;
+    pa::BlockMove m;
+    m.pairs = pairs;
+    m.block_bytes = blk;
+    m.src_blocks = src_blocks;
+    m.dst_blocks = dst_blocks;
+    for (int32_t l0 = 0; l0 < layers; l0 += pa::kMaxLayers) {
+        m.layers = layers - l0 < pa::kMaxLayers ? layers - l0 : pa::kMaxLayers;
+        for (int32_t l = 0; l < m.layers; ++l) {
+            m.src_k[l] = src_k[l0 + l];
+            m.src_v[l] = src_v[l0 + l];
+            m.dst_k[l] = dst_k[l0 + l];
+            m.dst_v[l] = dst_v[l0 + l];
+        }
+        const int e = pa::launch_move_blocks(m, n, stream);
+        if (e) return hip_status(e);
+    }
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,18 +224,24 @@ int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_
 
 int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int32_t num_pairs,
                    const pa_cache_params *p, void *stream) {
-    const int st = check_cache_params(p);
-    if (st != PA_OK) return st;
-    if (num_pairs < 0) return PA_ERR_SHAPE;
-    if (num_pairs == 0) return PA_OK;
-    if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
-    if (!aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_pairs & 3u))
-        return PA_ERR_ALIGN;
-    const int64_t blk = (int64_t)p->block_size * p->num_kv_heads * p->head_dim *
-                        elem_bytes(p->dtype);
-    const int e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, p->num_blocks,
-                                         blk, stream);
-    return hip_status(e);
+    void *k[1] = {k_cache}, *v[1] = {v_cache};
+    return pa_copy_blocks_layers(k, v, 1, block_pairs, num_pairs, p, stream);
+}
+
+int pa_copy_blocks_layers(void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                          const int32_t *block_pairs, int32_t num_pairs,
+                          const pa_cache_params *p, void *stream) {
+    return move_blocks(k_caches, v_caches, p ? p->num_blocks : 0, k_caches, v_caches,
+                       p ? p->num_blocks : 0, num_layers, block_pairs, num_pairs, p, stream);
+}
+
+int pa_swap_blocks(void *const *dst_k, void *const *dst_v, int32_t dst_num_blocks,
+                   const void *const *src_k, const void *const *src_v, int32_t src_num_blocks,
+                   int32_t num_layers, const int32_t *block_pairs, int32_t num_pairs,
+                   const pa_cache_params *p, void *stream) {
+    if (dst_num_blocks < 1 || src_num_blocks < 1) return PA_ERR_SHAPE;
+    return move_blocks(src_k, src_v, src_num_blocks, dst_k, dst_v, dst_num_blocks, num_layers,
+                       block_pairs, num_pairs, p, stream);
 }
 
 const char *pa_status_string(int status) {

@@ -678,7 +678,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
         const int nfull = (cte - ctb) / kStepTokens;
         const int tail = (cte - ctb) % kStepTokens;
 
-        // K and V of step j: lane loads token tok (clamped when MASKED).
+        // K and V of step j: lane loads token tok (clamped when MASKED).  Each
+        // load instruction covers 64 bytes of 16 rows (half of a 128-byte
+        // line each, the other half in the next instruction), so ordinary
+        // cached loads are used here: with the non-temporal hint this
+        // pattern ran ~10% slower.
         auto issue = [&]<bool MASKED>(vec4 (&kb_)[KL], vec4 (&vb_)[KL], int j) {
             const int t0 = ctb + j * kStepTokens;
             int r = tok;
@@ -696,8 +700,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
             }
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
-                kb_[i] = load_stream(kh + row + coff[i]);
-                vb_[i] = load_stream(vh + row + coff[i]);
+                kb_[i] = load_cached(kh + row + coff[i]);
+                vb_[i] = load_cached(vh + row + coff[i]);
             }
         };
         auto compute = [&]<bool MASKED>(const vec4 (&kb_)[KL], const vec4 (&vb_)[KL], int j) {
@@ -1135,39 +1139,53 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
     return (int)hipGetLastError();
 }
 
-// ---------------------------------------------------------------- copy_blocks
+// ---------------------------------------------------------------- block moves
 
-// Whole-block copies for every (src, dst) pair, K then V, in one launch
-// ([Kwon] §3.4 "Kernel-Level Optimizations", item 3).  A block is one
-// contiguous range in either pool layout.  Pairs naming a block outside
-// [0, NB) are skipped.
-__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
-    vec4 *__restrict__ k_cache, vec4 *__restrict__ v_cache, const int32_t *__restrict__ pairs,
-    int64_t total, int64_t bv, int32_t num_blocks) {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
-        const int64_t i = idx / (2 * bv);
-        const int64_t rem = idx - i * 2 * bv;
-        const bool is_v = rem >= bv;
-        const int64_t w = is_v ? rem - bv : rem;
-        const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
-        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) continue;
-        vec4 *pool = is_v ? v_cache : k_cache;
-        pool[(int64_t)dst * bv + w] = pool[(int64_t)src * bv + w];
+// Whole-block copies for every (src, dst) pair, K and V, for up to
+// kMaxLayers layers in one launch ([Kwon] §3.4 "Kernel-Level Optimizations",
+// item 3: one fused copy over all layers taking (source, destination)
+// pairs; "Scheduling and Preemption": swapping moves the same blocks
+// between the GPU pool and a host pool).  A block is one contiguous range in
+// either pool layout.  Grid: x = (pair, layer, K|V), y = 16 KiB chunks of
+// the block; each thread moves kMoveVecs 16-byte vectors, so the index
+// arithmetic is per workgroup and the loads of a thread are independent.
+// Source and destination pools may be device memory or device-accessible
+// pinned host memory.  Pairs naming a block outside either pool are skipped.
+constexpr int kMoveVecs = 4;
+
+__global__ __launch_bounds__(kThreads) void move_blocks_kernel(BlockMove m) {
+    const int64_t bv = m.block_bytes / 16;           // vectors per block
+    const uint32_t x = blockIdx.x;
+    const uint32_t kv = x & 1u;
+    const uint32_t pl = x >> 1;                       // pair * layers + layer
+    const uint32_t i = pl / (uint32_t)m.layers;
+    const uint32_t layer = pl - i * (uint32_t)m.layers;
+    const int32_t src = m.pairs[2 * i], dst = m.pairs[2 * i + 1];
+    if (src < 0 || src >= m.src_blocks || dst < 0 || dst >= m.dst_blocks) return;
+    const vec4 *from = reinterpret_cast<const vec4 *>(kv ? m.src_v[layer] : m.src_k[layer]) +
+                       (int64_t)src * bv;
+    vec4 *to = reinterpret_cast<vec4 *>(kv ? m.dst_v[layer] : m.dst_k[layer]) + (int64_t)dst * bv;
+    const int64_t w0 = (int64_t)blockIdx.y * (kThreads * kMoveVecs) + threadIdx.x;
+    vec4 r[kMoveVecs];
+#pragma unroll
+    for (int u = 0; u < kMoveVecs; ++u) {
+        const int64_t w = w0 + u * kThreads;
+        if (w < bv) r[u] = from[w];
+    }
+#pragma unroll
+    for (int u = 0; u < kMoveVecs; ++u) {
+        const int64_t w = w0 + u * kThreads;
+        if (w < bv) to[w] = r[u];
     }
 }
 
-int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t n,
-                       int32_t num_blocks, int64_t block_bytes, void *stream) {
-    const int64_t bv = block_bytes / 16;
-    const int64_t total = (int64_t)n * 2 * bv;
-    int64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
+int launch_move_blocks(const BlockMove &m, int32_t n, void *stream) {
+    const int64_t bv = m.block_bytes / 16;
+    const int64_t chunks = (bv + kThreads * kMoveVecs - 1) / (kThreads * kMoveVecs);
+    const int64_t gx = (int64_t)n * m.layers * 2;
     (void)hipGetLastError();  // an error left by other code is not this launch's
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       (hipStream_t)stream, (vec4 *)k_cache, (vec4 *)v_cache, pairs, total, bv,
-                       num_blocks);
+    hipLaunchKernelGGL(move_blocks_kernel, dim3((unsigned)gx, (unsigned)chunks), dim3(kThreads), 0,
+                       (hipStream_t)stream, m);
     return (int)hipGetLastError();
 }
 

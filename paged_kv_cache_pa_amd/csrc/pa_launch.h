@@ -32,8 +32,19 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                        const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
                        int32_t hkv, int64_t row_bytes, int32_t layout, void *stream);
 
-int launch_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int32_t n,
-                       int32_t num_blocks, int64_t block_bytes, void *stream);
+// Whole-block moves between two pools (or within one) for up to
+// kMaxLayers layers; passed by value as the kernel argument.
+constexpr int kMaxLayers = 64;
+struct BlockMove {
+    const void *src_k[kMaxLayers], *src_v[kMaxLayers];
+    void *dst_k[kMaxLayers], *dst_v[kMaxLayers];
+    const int32_t *pairs;    // [n][2] (src, dst), device-accessible
+    int64_t block_bytes;     // one block of one of K / V: B * Hkv * D * e
+    int32_t layers;          // 1 .. kMaxLayers
+    int32_t src_blocks, dst_blocks;
+};
+
+int launch_move_blocks(const BlockMove &m, int32_t n, void *stream);
 
 const char *hip_error_name(int err);
 const char *kernel_build_info();

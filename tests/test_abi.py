@@ -192,6 +192,39 @@ def test_cache_write_and_copy_pointer_checks(L):
     assert L.pa_cache_write(b.p, b.p, b.p, b.p, b.p, 3, None, None) == NULL
 
 
+def test_multi_layer_copy_and_swap_checks(L):
+    """Per-layer pointer arrays are checked entry by entry before any launch."""
+    b = Buf()
+    p = cparams()
+    P = ctypes.c_void_p
+
+    def arr(*xs):
+        return (P * len(xs))(*xs)
+
+    good = arr(b.p, b.p, b.p)
+    assert L.pa_copy_blocks_layers(good, good, 3, b.p, 0, ctypes.byref(p), None) == OK
+    assert L.pa_copy_blocks_layers(good, good, 0, b.p, 2, ctypes.byref(p), None) == SHAPE
+    assert L.pa_copy_blocks_layers(good, good, 3, b.p, -1, ctypes.byref(p), None) == SHAPE
+    assert L.pa_copy_blocks_layers(None, good, 3, b.p, 2, ctypes.byref(p), None) == NULL
+    assert L.pa_copy_blocks_layers(arr(b.p, None, b.p), good, 3, b.p, 2, ctypes.byref(p),
+                                   None) == NULL
+    assert L.pa_copy_blocks_layers(good, arr(b.p, b.p, b.odd), 3, b.p, 2, ctypes.byref(p),
+                                   None) == ALIGN
+    assert L.pa_copy_blocks_layers(good, good, 3, None, 2, ctypes.byref(p), None) == NULL
+    assert L.pa_copy_blocks_layers(good, good, 3, b.p, 2, ctypes.byref(cparams(dtype=9)),
+                                   None) == DTYPE
+    # too many (pair, layer, K|V) workgroups for one grid dimension
+    assert L.pa_copy_blocks_layers(good, good, 3, b.p, 1 << 30, ctypes.byref(p), None) == UNSUP
+    sw = L.pa_swap_blocks
+    assert sw(good, good, 8, good, good, 64, 3, b.p, 0, ctypes.byref(p), None) == OK
+    assert sw(good, good, 0, good, good, 64, 3, b.p, 2, ctypes.byref(p), None) == SHAPE
+    assert sw(good, good, 8, good, good, 0, 3, b.p, 2, ctypes.byref(p), None) == SHAPE
+    assert sw(good, None, 8, good, good, 64, 3, b.p, 2, ctypes.byref(p), None) == NULL
+    assert sw(good, good, 8, arr(b.odd, b.p, b.p), good, 64, 3, b.p, 2, ctypes.byref(p),
+              None) == ALIGN
+    assert sw(good, good, 8, good, good, 64, 3, P(b.p.value + 2), 2, ctypes.byref(p), None) == ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

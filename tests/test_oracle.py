@@ -464,6 +464,50 @@ def test_copy_blocks_matches_numpy(dtype):
     assert same_bits(kc, ke) and same_bits(vc, ve)
 
 
+@pytest.mark.parametrize("dtype", W.DTYPES)
+def test_swap_blocks_matches_byte_gather(dtype):
+    """Host <-> GPU pool moves: each destination block holds the source
+    block's bytes; ids outside either pool are skipped; a swap-out followed
+    by the reverse swap-in brings every moved block back unchanged."""
+    rng = np.random.default_rng(23)
+    L, B, H, D = 3, 8, 2, 32
+    gk = [W.randn(rng, (20, B, H, D), dtype) for _ in range(L)]
+    gv = [W.randn(rng, (20, B, H, D), dtype) for _ in range(L)]
+    hk = [W.randn(rng, (9, B, H, D), dtype) for _ in range(L)]
+    hv = [W.randn(rng, (9, B, H, D), dtype) for _ in range(L)]
+    pairs = np.array([[4, 0], [17, 8], [2, 3], [25, 1], [5, 9], [11, 5]], np.int32)
+    ok_, ov_ = oracle.swap_blocks(hk, hv, gk, gv, pairs)
+    valid = pairs[(pairs[:, 0] < 20) & (pairs[:, 1] < 9)]
+    for layer in range(L):
+        nbytes = gk[layer][0].nbytes
+        src = gk[layer].view(np.uint8).reshape(20, nbytes)
+        want = hk[layer].view(np.uint8).reshape(9, nbytes).copy()
+        want[valid[:, 1]] = src[valid[:, 0]]
+        assert np.array_equal(ok_[layer].view(np.uint8).reshape(9, nbytes), want)
+        untouched = np.setdiff1d(np.arange(9), valid[:, 1])
+        assert same_bits(ov_[layer][untouched], hv[layer][untouched])
+    # round trip: wipe the GPU blocks, then swap back in
+    wiped = [x.copy() for x in gk]
+    for layer in range(L):
+        wiped[layer][valid[:, 0]] = W.nan_fill(wiped[layer][valid[:, 0]].shape, dtype)
+    back_k, _ = oracle.swap_blocks(wiped, [x.copy() for x in gv], ok_, ov_, valid[:, ::-1])
+    for layer in range(L):
+        assert same_bits(back_k[layer], gk[layer])
+
+
+def test_copy_blocks_layers_is_per_layer_copy():
+    rng = np.random.default_rng(24)
+    ks = [W.randn(rng, (10, 4, 2, 16), "f16") for _ in range(4)]
+    vs = [W.randn(rng, (10, 4, 2, 16), "f16") for _ in range(4)]
+    pairs = np.array([[1, 7], [3, 2]], np.int32)
+    kc, vc = oracle.copy_blocks_layers(ks, vs, pairs, "f16")
+    for layer in range(4):
+        ke, ve = ks[layer].copy(), vs[layer].copy()
+        ke[[7, 2]] = ks[layer][[1, 3]]
+        ve[[7, 2]] = vs[layer][[1, 3]]
+        assert same_bits(kc[layer], ke) and same_bits(vc[layer], ve)
+
+
 def test_index_errors_write_nothing():
     k, v = empty_pool(4, 4, 1, 8, "f32")
     new = np.ones((2, 1, 8), np.float32)
