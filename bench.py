@@ -339,6 +339,80 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+BLOCK_SWEEP_SIZES = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def block_sweep(rounds=10, seqs=16, ctx=4096, hq=12, hkv=2, d=128, partition=256):
+    """Decode time against block size, blocks in order and scattered, against
+    the contiguous twin, on the shape of [Res] "Attention over scattered
+    blocks" (16 sequences x 4096 cached tokens, 12 query / 2 kv heads, head
+    dim 128, fp16: 64 MiB of K and V per step; head-major pools).  The
+    identical values sit in every layout: the dense [S, Hkv, ctx, D] buffer
+    is cut into blocks of B tokens, which are placed in order or by a seeded
+    permutation.  Split into partitions of ``partition`` tokens so the
+    16 x 2 (sequence, kv head) pairs fill the GPU.  One JSON line per point;
+    times are per launch over rotating replicas (decode + merge)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(606)
+    per = seqs * hkv * ctx * d * 2 * 2  # K + V bytes
+    R = replicas_for(per)
+    dense = [(torch.randn((seqs, hkv, ctx, d), generator=g, device="cuda").half(),
+              torch.randn((seqs, hkv, ctx, d), generator=g, device="cuda").half())
+             for _ in range(R)]
+    q = torch.randn((seqs, hq, d), generator=g, device="cuda").half()
+    cl = torch.full((seqs,), ctx, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    scale = 1.0 / np.sqrt(d)
+    nbytes = decode_bytes(np.full(seqs, ctx), hq, hkv, d, 2, 16) - 4 * seqs * ctx // 16
+
+    def timed(f):
+        for i in range(2 * R):
+            f(i)
+        return float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+
+    def f_dense(i):
+        k, v = dense[i % R]
+        pa.pa_decode_dense(q, k, v, cl, scale, out, max_context_len=ctx,
+                           partition_size=partition, layout="HND")
+
+    t_dense = timed(f_dense)
+    print(json.dumps({"config": "block sweep", "block_size": None, "placement": "contiguous",
+                      "us": round(t_dense * 1e6, 2), "GB_s": round(nbytes / t_dense / 1e9, 1),
+                      "replicas": R}), flush=True)
+    rng = np.random.default_rng(606)
+    for B in BLOCK_SWEEP_SIZES:
+        nb_seq = ctx // B
+        nb = seqs * nb_seq
+        for placement in ("in order", "scattered"):
+            ids = np.arange(nb) if placement == "in order" else rng.permutation(nb)
+            # block j of sequence s holds tokens [j B, (j + 1) B) of the dense buffer
+            table = ids.reshape(seqs, nb_seq).astype(np.int32)
+            bt = torch.from_numpy(table).cuda()
+            inv = torch.from_numpy(np.argsort(ids)).cuda()  # pool slot -> (s, j) in order
+            pools = []
+            for k, v in dense:
+                def blocks(x):
+                    x = x.view(seqs, hkv, nb_seq, B, d).permute(0, 2, 1, 3, 4)
+                    return x.reshape(nb, hkv, B, d)[inv].contiguous()
+                pools.append((blocks(k), blocks(v)))
+
+            def f_paged(i):
+                k, v = pools[i % R]
+                pa.pa_decode(q, k, v, bt, cl, scale, out, max_context_len=ctx,
+                             partition_size=partition, layout="HND")
+
+            t = timed(f_paged)
+            print(json.dumps({"config": "block sweep", "block_size": B, "placement": placement,
+                              "us": round(t * 1e6, 2), "vs_contiguous": round(t / t_dense, 3),
+                              "GB_s": round(nbytes / t / 1e9, 1), "replicas": R}), flush=True)
+            del pools
+            torch.cuda.empty_cache()
+
+
 def sweep(rounds=10):
     """Every configuration's kernels, timed over rotating replicas (one JSON
     object per line; not the benchmark's contract line)."""
@@ -635,6 +709,9 @@ def main():
                     help="skip the dense ratio, copy_blocks and CPU legs (for profiling runs)")
     ap.add_argument("--counters-run", action="store_true",
                     help="short run for rocprofv3 --pmc passes (decode launches + calibration copy)")
+    ap.add_argument("--block-sweep", action="store_true",
+                    help="decode time against block size (1..256), in order / scattered / "
+                         "contiguous, on a 16 x 4096-token GQA batch; one JSON line per point")
     ap.add_argument("--sweep", action="store_true",
                     help="time every configuration's kernels (JSON lines, not the contract line)")
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
@@ -662,6 +739,9 @@ def main():
         return
     if args.sweep:
         sweep()
+        return
+    if args.block_sweep:
+        block_sweep()
         return
     dev = torch.device("cuda:0")
     t_gen = time.time()

@@ -1035,15 +1035,19 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
         fn = l.dense ? decode_mma_kernel<T, D, G, kDense>
            : l.B >= kStepTokens ? decode_mma_kernel<T, D, G, kPagedWide>
                                 : decode_mma_kernel<T, D, G, kPagedNarrow>;
-        nw = pick_waves((const void *)fn, (const void *)fn, wgs, lds_of(8), lds_of(4));
+        // The wave count follows one instantiation for every address mode, so
+        // paged and dense launches of one shape split the work identically
+        // (and give identical bits).
+        const void *ref = (const void *)decode_mma_kernel<T, D, G, kPagedWide>;
+        nw = pick_waves(ref, ref, wgs, lds_of(8), lds_of(4));
         lds = lds_of(nw);
     } else {
         auto lds_of = [&](int w) { return max2((size_t)kTableChunk * 4, red_bytes(w)); };
         fn = l.dense ? decode_kernel<T, D, G, kDense>
            : l.B >= kStepTokens ? decode_kernel<T, D, G, kPagedWide>
                                 : decode_kernel<T, D, G, kPagedNarrow>;
-        nw = pick_waves(max_waves<T>() >= 8 ? (const void *)fn : nullptr, (const void *)fn, wgs,
-                        lds_of(8), lds_of(4));
+        const void *ref = (const void *)decode_kernel<T, D, G, kPagedWide>;
+        nw = pick_waves(max_waves<T>() >= 8 ? ref : nullptr, ref, wgs, lds_of(8), lds_of(4));
         lds = lds_of(nw);
     }
     (void)hipGetLastError();  // an error left by other code is not this launch's
