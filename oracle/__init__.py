@@ -54,12 +54,13 @@ def load(path):
     L.oracle_decode_split.argtypes = [P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, I, P, I]
     L.oracle_cache_write.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I]
     L.oracle_copy_blocks.argtypes = [P, P, P, I, I, I, I, I, I]
+    L.oracle_prefill.argtypes = [P, P, P, P, P, P, D, I, I, I, I, I, I, I, I, I, I, P, I]
     L.oracle_half_to_double.argtypes = [ctypes.c_uint16]
     L.oracle_half_to_double.restype = D
     L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
     L.oracle_bf16_to_double.restype = D
     for f in ("oracle_decode", "oracle_decode_dense", "oracle_decode_split",
-              "oracle_cache_write", "oracle_copy_blocks"):
+              "oracle_cache_write", "oracle_copy_blocks", "oracle_prefill"):
         getattr(L, f).restype = I
     return L
 
@@ -151,6 +152,26 @@ def decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, dtype,
                                    float(scale), S, Hq, Hkv, D, B, bt.shape[1], NB, _DT[dtype],
                                    _LAYOUT[layout], int(partition_size), _ptr(out), _threads(nthreads))
     _check(rc, "oracle_decode_split")
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, dtype,
+            nthreads=None, layout="NHD"):
+    """Multi-token queries in fp64: q [rows, Hq, D]; sequence s owns rows
+    query_start[s] .. query_start[s+1]-1, the last of its context_lens[s]
+    cached tokens, and row r of its chunk attends causally to tokens
+    0 .. n - T + r.  Returns out [rows, Hq, D] (float64)."""
+    q, k_cache, v_cache = _c(q), _c(k_cache), _c(v_cache)
+    bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    qs = _c(query_start, np.int32)
+    T, Hq, D = q.shape
+    S = cl.shape[0]
+    NB, B, Hkv, _ = _dims(k_cache, layout)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    rc = lib().oracle_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl), _ptr(qs),
+                              float(scale), S, Hq, Hkv, D, B, bt.shape[1], NB, T, _DT[dtype],
+                              _LAYOUT[layout], _ptr(out), _threads(nthreads))
+    _check(rc, "oracle_prefill")
     return out
 
 

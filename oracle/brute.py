@@ -64,3 +64,32 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale, widen=float):
         out.append(row_o)
         weights.append(row_a)
     return out, weights
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, widen=float):
+    """Multi-token queries, one scalar at a time: q [rows][Hq][D]; sequence s
+    owns rows query_start[s] .. query_start[s+1]-1, the last T of its n
+    cached tokens; the chunk's r-th row sits at position n - T + r and
+    attends to positions 0 .. n - T + r.  Returns out [rows][Hq][D]."""
+    Hq = len(q[0])
+    B = len(k_cache[0])
+    Hkv = len(k_cache[0][0])
+    G = Hq // Hkv
+    out = [None] * len(q)
+    for s in range(len(context_lens)):
+        n = int(context_lens[s])
+        lo, hi = int(query_start[s]), int(query_start[s + 1])
+        for i in range(lo, hi):
+            visible = n - (hi - lo) + (i - lo) + 1
+            row = []
+            for h in range(Hq):
+                g = h // G
+                keys, vals = [], []
+                for t in range(visible):
+                    b, off = resolve(block_tables[s], t, B)
+                    keys.append([widen(x) for x in k_cache[b][off][g]])
+                    vals.append([widen(x) for x in v_cache[b][off][g]])
+                o, _ = attend_one([widen(x) for x in q[i][h]], keys, vals, scale)
+                row.append(o)
+            out[i] = row
+    return out

@@ -391,3 +391,71 @@ int oracle_copy_blocks(void *k_cache, void *v_cache, const int32_t *pairs, int n
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* multi-token queries: a chunk of new tokens per sequence             */
+
+/* Prefill / chunked prefill over the paged cache ([Kwon] §3.4: the prompt
+ * phase computes attention for all prompt tokens at once, each token
+ * attending to itself and the tokens before it; the paged kernel reads keys
+ * and values through the block table).  Sequence s owns query rows
+ * query_start[s] .. query_start[s+1]-1 (T_s rows), the LAST T_s of its
+ * context_lens[s] cached tokens, whose keys and values are already in the
+ * pool.  Row r of the chunk sits at position pos = n - T_s + r and attends
+ * to cached tokens 0 .. pos (causal), with the same softmax as decode.
+ * q, out: [total_rows, Hq, D]; out is fp64. */
+int oracle_prefill(const void *q, const void *k_cache, const void *v_cache,
+                   const int32_t *block_tables, const int32_t *context_lens,
+                   const int32_t *query_start, double scale, int S, int Hq, int Hkv, int D,
+                   int B, int MBS, int NB, int total_rows, int dtype, int layout,
+                   double *out, int nthreads) {
+    if (check_shape(S, Hq, Hkv, D, dtype) || B <= 0 || MBS <= 0 || NB <= 0) return -1;
+    if ((layout != 0 && layout != 1) || total_rows < 0) return -1;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return -1;
+    if (query_start[0] != 0 || query_start[S] != total_rows) return -1;
+    for (int s = 0; s < S; ++s) {
+        int rows = query_start[s + 1] - query_start[s];
+        int len = context_lens[s];
+        if (rows < 0 || len < rows || len > MBS * B) return -1;
+        for (int j = 0; j < (len + B - 1) / B; ++j) {
+            int32_t id = block_tables[(size_t)s * MBS + j];
+            if (id < 0 || id >= NB) return -2;
+        }
+    }
+    const int group = Hq / Hkv;
+    int status = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(min : status)
+#endif
+    for (int unit = 0; unit < S * Hq; ++unit) {
+        const int seq = unit / Hq, head = unit % Hq;
+        const int kv = head / group;
+        const int len = context_lens[seq];
+        const int first = query_start[seq], rows = query_start[seq + 1] - first;
+        if (rows == 0) continue;
+        double *Kc = malloc((size_t)len * D * sizeof(double));
+        double *Vc = malloc((size_t)len * D * sizeof(double));
+        double *scratch = malloc((size_t)len * sizeof(double));
+        double *qrow = malloc((size_t)D * sizeof(double));
+        if (!Kc || !Vc || !scratch || !qrow) {
+            status = -1;
+        } else {
+            const int32_t *trow = block_tables + (size_t)seq * MBS;
+            if (gather_seq(k_cache, trow, len, B, NB, Hkv, D, kv, dtype, layout, Kc) ||
+                gather_seq(v_cache, trow, len, B, NB, Hkv, D, kv, dtype, layout, Vc)) {
+                status = -2;
+            } else {
+                for (int r = 0; r < rows; ++r) {
+                    const size_t at = ((size_t)(first + r) * Hq + head) * D;
+                    const int pos = len - rows + r;   /* this row's position */
+                    for (int d = 0; d < D; ++d) qrow[d] = load(q, at + d, dtype);
+                    attend(qrow, Kc, Vc, pos + 1, D, scale, out + at, NULL, scratch);
+                }
+            }
+        }
+        free(Kc); free(Vc); free(scratch); free(qrow);
+    }
+    return status;
+}

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import test_oracle as T
+import test_oracle_prefill as TP
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -42,11 +43,20 @@ MUTANTS = [
     ("copy_direction", "memmove((char *)k_cache + dst, (const char *)k_cache + src, blk);",
      "memmove((char *)k_cache + src, (const char *)k_cache + dst, blk);",
      ["test_copy_blocks_matches_numpy", "test_internals_cow_trace"]),
+    ("prefill_position_off_by_one", "const int pos = len - rows + r;",
+     "const int pos = len - rows + r - 1;",
+     ["prefill:test_last_row_is_decode", "prefill:test_matches_numpy_masked_softmax"]),
+    ("prefill_not_causal", "attend(qrow, Kc, Vc, pos + 1, D, scale, out + at, NULL, scratch);",
+     "attend(qrow, Kc, Vc, len, D, scale, out + at, NULL, scratch);",
+     ["prefill:test_causal_future_tokens_do_not_matter",
+      "prefill:test_single_row_at_position_is_decode_of_prefix"]),
+    ("prefill_wrong_kv_head", "const int kv = head / group;", "const int kv = head % Hkv;",
+     ["prefill:test_matches_numpy_masked_softmax"]),
 ]
 
 
 def _run(name, golden):
-    fn = getattr(T, name)
+    fn = getattr(TP, name.split(":", 1)[1]) if name.startswith("prefill:") else getattr(T, name)
     import inspect
 
     params = inspect.signature(fn).parameters

@@ -450,3 +450,41 @@ def config3_device(batch, ctx, seed=303, device="cuda"):
     lens = torch.full((batch,), ctx, dtype=torch.int32, device=device)
     return dict(q=q, k_cache=k, v_cache=v, block_tables=table, context_lens=lens,
                 k_dense=k_dense, v_dense=v_dense, scale=1.0 / math.sqrt(D))
+
+
+@dataclasses.dataclass
+class Prefill:
+    """Multi-token queries over a paged cache: sequence s owns query rows
+    query_start[s] .. query_start[s+1]-1, the last chunk_lens[s] of its
+    context_lens[s] cached tokens (their K/V already in the pool)."""
+    dtype: str
+    q: np.ndarray               # [rows, Hq, D]
+    k_cache: np.ndarray         # [NB, B, Hkv, D] token-major
+    v_cache: np.ndarray
+    block_tables: np.ndarray    # [S, MBS] int32
+    context_lens: np.ndarray    # [S] int32
+    query_start: np.ndarray     # [S + 1] int32
+    scale: float
+    block_size: int
+    name: str = ""
+
+    @property
+    def chunk_lens(self):
+        return np.diff(self.query_start).astype(np.int32)
+
+
+def random_prefill(seed, dtype, ctx_lens, chunk_lens, hq, hkv, d, block_size=16,
+                   extra_blocks=3, poison=True, scale=None) -> Prefill:
+    """Seeded pool and queries for a batch of chunks: placement and pool as
+    random_paged, then one N(0,1) query row per chunk token."""
+    ctx_lens = np.asarray(ctx_lens, dtype=np.int32)
+    chunk_lens = np.asarray(chunk_lens, dtype=np.int32)
+    assert np.all(chunk_lens <= ctx_lens) and np.all(chunk_lens >= 0)
+    p = random_paged(seed, dtype, ctx_lens, hq, hkv, d, block_size=block_size,
+                     extra_blocks=extra_blocks, poison=poison, scale=scale)
+    rng = np.random.default_rng(seed + 7919)
+    qs = np.zeros(len(chunk_lens) + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(chunk_lens)
+    q = randn(rng, (int(qs[-1]), hq, d), dtype)
+    return Prefill(dtype, q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, qs, p.scale,
+                   block_size, name=f"prefill-{dtype}-s{seed}")
