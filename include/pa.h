@@ -237,6 +237,46 @@ int pa_swap_blocks(void *const *dst_k, void *const *dst_v, int32_t dst_num_block
                    int32_t num_layers, const int32_t *block_pairs, int32_t num_pairs,
                    const pa_cache_params *p, void *stream);
 
+/*
+ * prefill: attention for a chunk of new tokens per sequence over the paged
+ * cache -- the prompt phase, and chunked prefill where a long prompt arrives
+ * in pieces ([Kwon] §3.4 "PagedAttention Algorithm" and the prompt phase of
+ * §2: each prompt token attends to itself and every earlier token; the keys
+ * and values are read through the block table).  Sequence s owns the query
+ * rows query_start[s] .. query_start[s+1] - 1 (T_s rows), which are the
+ * LAST T_s of its context_lens[s] cached tokens: their keys and values must
+ * already be in the pool (pa_cache_write).  Chunk row r sits at position
+ * n_s - T_s + r and attends to positions 0 .. n_s - T_s + r, with the
+ * decode softmax and scale.
+ * Layouts: q, out [total_query_rows, Hq, D]; pools and tables as pa_decode;
+ * query_start [num_seqs + 1] int32, query_start[0] = 0, non-decreasing,
+ * query_start[num_seqs] = total_query_rows.  Device pointers.
+ * Host-checked: dtype fp16 or bf16 (fp32: PA_ERR_UNSUPPORTED), head_dim 64
+ * or 128, Hq a multiple of Hkv, block_size a power of two in [1, 256],
+ * max_context_len <= max_blocks_per_seq * block_size, 16-byte aligned q,
+ * caches and out, 4-byte aligned int arrays.
+ * Preconditions (device data, not checked): 0 <= T_s <= max_query_len,
+ * T_s <= context_lens[s] <= max_context_len, table entries of the first
+ * ceil(n / B) blocks in [0, NB).  Violations never cause an out-of-range
+ * access (rows, lengths and ids are clamped); the rows concerned are then
+ * unspecified.
+ */
+typedef struct {
+    int32_t num_seqs;
+    int32_t num_q_heads, num_kv_heads, head_dim;
+    int32_t block_size, max_blocks_per_seq, num_blocks;
+    int32_t total_query_rows;   /* rows of q and out */
+    int32_t max_query_len;      /* bound on every chunk length; sizes the grid */
+    int32_t max_context_len;    /* bound on every context length */
+    int32_t dtype;              /* pa_dtype: PA_F16 or PA_BF16 */
+    int32_t layout;             /* pa_kv_layout */
+} pa_prefill_params;
+
+int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, float scale, void *out,
+               const pa_prefill_params *p, void *stream);
+
 /* Static text for a pa_status value (never NULL). */
 const char *pa_status_string(int status);
 

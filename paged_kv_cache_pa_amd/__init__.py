@@ -8,7 +8,7 @@ is not built, every call raises.
 
 Entry points (same names as the C ABI):
   pa_decode, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
-  pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks
+  pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
 and the host block manager (``include/pa_block_manager.h``) as the class
 ``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
 """
@@ -20,7 +20,8 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["pa_decode", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
-           "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "PaError", "lib",
+           "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill", "PaError",
+           "lib",
            "LIB_PATH", "STATUS"]
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
@@ -43,6 +44,13 @@ class DecodeParams(ctypes.Structure):
         "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
         "max_blocks_per_seq", "num_blocks", "max_context_len", "partition_size", "dtype",
         "layout")]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_seqs", "num_q_heads", "num_kv_heads", "head_dim", "block_size",
+        "max_blocks_per_seq", "num_blocks", "total_query_rows", "max_query_len",
+        "max_context_len", "dtype", "layout")]
 
 
 class CacheParams(ctypes.Structure):
@@ -91,9 +99,11 @@ def lib():
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I32, CP, P]
         L.pa_copy_blocks_layers.argtypes = [P, P, I32, P, I32, CP, P]
+        L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
+                                 ctypes.POINTER(PrefillParams), P]
         L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
         for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_dense", "pa_cache_write",
-                  "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks"):
+                  "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
@@ -328,3 +338,38 @@ def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None, layo
                                 _ptr_array(src_k), _ptr_array(src_v), ps.num_blocks,
                                 len(src_k), _ptr(block_pairs), int(block_pairs.shape[0]),
                                 ctypes.byref(ps), _stream(stream)), "pa_swap_blocks")
+
+
+def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out, *,
+               max_query_len=None, max_context_len=None, stream=None, layout="NHD"):
+    """Multi-token (prompt / chunked-prefill) attention over the paged cache;
+    writes ``out`` [rows, Hq, D] and returns it.  Sequence s owns q rows
+    query_start[s] .. query_start[s+1]-1, the last of its context_lens[s]
+    cached tokens; row r of its chunk attends causally.  ``max_query_len``
+    and ``max_context_len`` are host-known bounds (default: all rows / the
+    table capacity)."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4, q.dtype)
+    _need(v_cache, "v_cache", 4, q.dtype)
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(query_start, "query_start", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch between k_cache/v_cache or q/out")
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables [S, MBS], context_lens [S], query_start [S + 1]")
+    NB, B, Hkv, D = pool_dims(k_cache, layout)
+    MBS = block_tables.shape[1]
+    rows = q.shape[0]
+    p = PrefillParams(S, q.shape[1], Hkv, D, B, MBS, NB, rows,
+                      rows if max_query_len is None else int(max_query_len),
+                      MBS * B if max_context_len is None else int(max_context_len),
+                      _dtype_code(q), _layout(layout))
+    _check(lib().pa_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                            _ptr(context_lens), _ptr(query_start), float(scale), _ptr(out),
+                            ctypes.byref(p), _stream(stream)), "pa_prefill")
+    return out

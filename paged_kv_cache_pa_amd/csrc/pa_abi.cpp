@@ -222,6 +222,59 @@ int pa_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_
     return hip_status(e);
 }
 
+int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, const int32_t *context_lens,
+               const int32_t *query_start, float scale, void *out,
+               const pa_prefill_params *p, void *stream) {
+    if (!p) return PA_ERR_NULL;
+    if (!dtype_ok(p->dtype)) return PA_ERR_DTYPE;
+    if (p->num_seqs < 0 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1 ||
+        p->total_query_rows < 0 || p->max_query_len < 0 || p->max_context_len < 0)
+        return PA_ERR_SHAPE;
+    if (p->num_q_heads % p->num_kv_heads) return PA_ERR_SHAPE;
+    if (!layout_ok(p->layout)) return PA_ERR_SHAPE;
+    if (!pow2_in(p->block_size, 1, 256)) return PA_ERR_SHAPE;
+    if (p->max_blocks_per_seq < 1 || p->num_blocks < 1) return PA_ERR_SHAPE;
+    if (p->max_context_len > (int64_t)p->max_blocks_per_seq * p->block_size) return PA_ERR_SHAPE;
+    if (p->max_query_len > p->max_context_len) return PA_ERR_SHAPE;
+    if (p->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
+    if (p->num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
+    const int64_t tiles = ((int64_t)p->max_query_len + 63) / 64;
+    if ((int64_t)p->num_seqs * tiles > 0x7FFFFFFF / 256) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)p->total_query_rows * p->num_q_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+    if (p->num_seqs == 0 || p->total_query_rows == 0 || p->max_query_len == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+        return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return PA_ERR_ALIGN;
+    if (((uintptr_t)block_tables & 3u) || ((uintptr_t)context_lens & 3u) ||
+        ((uintptr_t)query_start & 3u))
+        return PA_ERR_ALIGN;
+    pa::PrefillLaunch l;
+    l.q = q;
+    l.k = k_cache;
+    l.v = v_cache;
+    l.tables = block_tables;
+    l.lens = context_lens;
+    l.qstart = query_start;
+    l.out = out;
+    l.scale = scale;
+    l.S = p->num_seqs;
+    l.Hq = p->num_q_heads;
+    l.Hkv = p->num_kv_heads;
+    l.D = p->head_dim;
+    l.dtype = p->dtype;
+    l.B = p->block_size;
+    l.MBS = p->max_blocks_per_seq;
+    l.NB = p->num_blocks;
+    l.max_ctx = p->max_context_len;
+    l.max_q = p->max_query_len;
+    l.total_rows = p->total_query_rows;
+    l.layout = p->layout;
+    return hip_status(pa::launch_prefill(l, stream));
+}
+
 int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int32_t num_pairs,
                    const pa_cache_params *p, void *stream) {
     void *k[1] = {k_cache}, *v[1] = {v_cache};

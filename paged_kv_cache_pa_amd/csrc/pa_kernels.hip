@@ -1091,6 +1091,238 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
     return (int)e;
 }
 
+// ---------------------------------------------------------------- prefill
+
+// Multi-token queries over the paged cache: prompt and chunked-prefill
+// attention ([Kwon] §3.4: in the prompt phase every token attends to itself
+// and the tokens before it, and the paged kernel reads keys and values
+// through the block table).  Sequence s owns query rows qstart[s] ..
+// qstart[s+1]-1, the last T of its n cached tokens (their keys and values
+// are already in the pool); chunk row r sits at position n - T + r and
+// attends to positions 0 .. n - T + r.
+//
+// One workgroup of 4 waves per (sequence, 64-row tile of its chunk, query
+// head); each wave owns 16 query rows.  The workgroup walks the keys in
+// 16-token tiles: each thread loads one 16-byte piece of the next tile's K
+// and V rows into registers, the tile is written to one of two LDS buffers,
+// and every wave computes its 16 x 16 score tile on matrix cores as
+// S^T = K Q^T (K from LDS as the A operand, Q^T held in registers), updates
+// its running softmax per query column, and accumulates O^T += V^T P^T with
+// V^T read from LDS by the transposing ds_read_b64_tr_b16 (lane l addresses
+// row l / 4, columns d0 + 4 (l % 4), and receives V[4 (l / 16) + j][d0 + l %
+// 16], the A-operand layout) and P^T reused in place as the B operand.  The
+// causal mask and the chunk's end are applied per score.  fp16 and bf16.
+struct PrefillArgs {
+    const char *q, *k, *v;
+    const int32_t *tables, *lens, *qstart;
+    void *out;
+    float qk_scale;  // scale * log2(e)
+    int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, max_q, total_rows, tiles;
+    int64_t tok_bytes, head_bytes, blk_bytes;
+};
+
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRows = 16 * kPrefillWaves;  // query rows per workgroup
+
+typedef short short4_t2 __attribute__((ext_vector_type(4)));
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
+    using E = Elem<T>;
+    using M = Mma<T>;
+    constexpr int KL = D / 32;           // 32-dim slices of the score product
+    constexpr int DS = D / 16;           // 16-dim slices of the output
+    constexpr int ROW = D * 2 + 16;      // padded LDS row of a K or V tile (bytes)
+    constexpr int TILE = 16 * ROW;
+    constexpr int CPR = D * 2 / 16;      // 16-byte pieces per row
+    constexpr int LOADERS = 16 * CPR;    // threads that load one tile (<= 256)
+    static_assert(LOADERS <= kPrefillWaves * 64, "one piece per thread");
+
+    __shared__ int32_t s_tab[kTableChunk];
+    __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE];  // [buffer][K|V][tile]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15;  // key row of the A operand; query column of the scores
+    const int kb = lane >> 4;   // k-block of the operands; 4-key group of the scores
+    const int s = blockIdx.x / a.tiles;
+    const int tile = blockIdx.x - s * a.tiles;
+    const int h = blockIdx.y;
+    const int g = h / (a.Hq / a.Hkv);
+
+    // The chunk's rows, clamped so that no access leaves q, out or the table.
+    int q0 = a.qstart[s], q1 = a.qstart[s + 1];
+    q0 = q0 < 0 ? 0 : (q0 > a.total_rows ? a.total_rows : q0);
+    q1 = q1 < q0 ? q0 : (q1 > a.total_rows ? a.total_rows : q1);
+    const int n = clamp_len(a.lens[s], a.max_ctx);
+    int rows = q1 - q0;  // chunk length
+    rows = rows > a.max_q ? a.max_q : rows;
+    rows = rows > n ? n : rows;
+    const int tr0 = tile * kPrefillRows;
+    if (tr0 >= rows) return;  // the whole workgroup idles
+    const int r0 = tr0 + 16 * wave;
+    const int rows_w = rows - r0 < 0 ? 0 : (rows - r0 > 16 ? 16 : rows - r0);
+    const int my_pos = n - rows + r0 + col;                       // this lane's query position
+    const int w_last = rows_w ? n - rows + r0 + rows_w - 1 : -1;  // last key of this wave
+    const int nkeys = n - rows + (tr0 + kPrefillRows < rows ? tr0 + kPrefillRows : rows);  // of the WG
+
+    // B operand of S^T = K Q^T: query row r0 + col, dims 32 i + 8 kb .. + 7.
+    const int64_t qrow = (int64_t)(q0 + r0 + col) * a.Hq + h;
+    vec4 qb[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+        qb[i] = col < rows_w ? load_cached(a.q + (qrow * D + 32 * i + 8 * kb) * 2)
+                             : vec4{0u, 0u, 0u, 0u};
+
+    float m = kNegBig, lsum = 0.0f;
+    float4_t acc[DS];
+#pragma unroll
+    for (int d = 0; d < DS; ++d) acc[d] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int B = 1 << a.log2B;
+    const int32_t *trow = a.tables + (int64_t)s * a.MBS;
+    const int64_t head0 = (int64_t)g * a.head_bytes;
+    const int lkey = tid / CPR, lpiece = tid % CPR;  // this thread's piece of a tile
+    const bool loader = tid < LOADERS;
+    const int nblk = (nkeys + B - 1) >> a.log2B;
+
+    for (int cb = 0; cb < nblk; cb += kTableChunk) {
+        const int cn = nblk - cb < kTableChunk ? nblk - cb : kTableChunk;
+        const int ck0 = cb << a.log2B;
+        const int ck1 = (cb + cn) << a.log2B < nkeys ? (cb + cn) << a.log2B : nkeys;
+        const int nst = (ck1 - ck0 + 15) >> 4;
+        __syncthreads();  // the previous chunk's readers are done
+        stage_table(trow, cb, cn, a.NB, s_tab, tid, blockDim.x);
+        __syncthreads();
+
+        vec4 kr, vr;
+        auto fetch = [&](int j) {  // this thread's piece of tile j (clamped to a real key)
+            int t = ck0 + 16 * j + lkey;
+            t = t < ck1 ? t : ck1 - 1;
+            const int64_t row = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
+                                (int64_t)(t & (B - 1)) * a.tok_bytes + head0 + lpiece * 16;
+            kr = load_cached(a.k + row);
+            vr = load_cached(a.v + row);
+        };
+        auto stash = [&](int buf) {
+            *reinterpret_cast<vec4 *>(&s_kv[buf][0][lkey * ROW + lpiece * 16]) = kr;
+            *reinterpret_cast<vec4 *>(&s_kv[buf][1][lkey * ROW + lpiece * 16]) = vr;
+        };
+        if (loader) {
+            fetch(0);
+            stash(0);
+        }
+        __syncthreads();
+        for (int j = 0; j < nst; ++j) {
+            const int buf = j & 1;
+            if (loader && j + 1 < nst) fetch(j + 1);  // in flight during this tile's math
+            const int key0 = ck0 + 16 * j;
+            if (key0 <= w_last) {  // wave-uniform: tiles past this wave's rows are skipped
+                const char *kt = s_kv[buf][0];
+                const char *vt = s_kv[buf][1];
+                float4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < KL; ++i) {
+                    const vec4 ka = *reinterpret_cast<const vec4 *>(kt + col * ROW + (32 * i + 8 * kb) * 2);
+                    sc = M::qk(ka, qb[i], sc);
+                }
+                float x[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int key = key0 + 4 * kb + jj;
+                    x[jj] = (key > my_pos || key >= ck1) ? -__builtin_inff() : sc[jj] * a.qk_scale;
+                }
+                float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mn = fmaxf(m, mx);
+                const float alpha = fexp2(m - mn);
+                float p[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[jj] - mn);
+                lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+                m = mn;
+                const vec2 pb = M::pack(p[0], p[1], p[2], p[3]);
+                const vec2 pr = M::rest(p[0], p[1], p[2], p[3], pb);
+#pragma unroll
+                for (int d = 0; d < DS; ++d) {
+                    // A operand of O^T += V^T P^T through the transposing read
+                    const char *src = vt + (lane >> 2) * ROW + (16 * d + 4 * (lane & 3)) * 2;
+                    const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (short4_t2 __attribute__((address_space(3))) *)(src));
+                    const vec2 va = __builtin_bit_cast(vec2, t4);
+                    acc[d] = acc[d] * alpha;
+                    acc[d] = M::pv(va, pb, acc[d]);
+                    if constexpr (M::kSplit) acc[d] = M::pv(va, pr, acc[d]);
+                }
+            }
+            if (loader && j + 1 < nst) stash(buf ^ 1);
+            __syncthreads();  // tile j + 1 is in place; tile j's readers are done
+        }
+    }
+
+    // The four lanes of a query column (col, col + 16, col + 32, col + 48)
+    // hold the same running max and partial sums over their keys.
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (col < rows_w) {
+        const float inv = 1.0f / lsum;
+        const int64_t o = qrow * D;
+#pragma unroll
+        for (int d = 0; d < DS; ++d)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) E::store(a.out, o + 16 * d + 4 * kb + jj, acc[d][jj] * inv);
+    }
+}
+
+template <typename T>
+static hipError_t launch_prefill_t(const PrefillLaunch &l, hipStream_t st) {
+    PrefillArgs a;
+    a.q = (const char *)l.q;
+    a.k = (const char *)l.k;
+    a.v = (const char *)l.v;
+    a.tables = l.tables;
+    a.lens = l.lens;
+    a.qstart = l.qstart;
+    a.out = l.out;
+    a.qk_scale = l.scale * kLog2e;
+    a.S = l.S;
+    a.Hq = l.Hq;
+    a.Hkv = l.Hkv;
+    a.NB = l.NB;
+    a.MBS = l.MBS;
+    int lb = 0;
+    while ((1 << lb) < l.B) ++lb;
+    a.log2B = lb;
+    a.max_ctx = l.max_ctx;
+    a.max_q = l.max_q;
+    a.total_rows = l.total_rows;
+    a.tiles = (l.max_q + kPrefillRows - 1) / kPrefillRows;
+    const int64_t row = (int64_t)l.D * sizeof(T);
+    if (l.layout == 0) {
+        a.tok_bytes = row * l.Hkv;
+        a.head_bytes = row;
+    } else {
+        a.tok_bytes = row;
+        a.head_bytes = row * l.B;
+    }
+    a.blk_bytes = row * l.Hkv * l.B;
+    const dim3 grid((unsigned)((int64_t)l.S * a.tiles), (unsigned)l.Hq);
+    (void)hipGetLastError();  // an error left by other code is not this launch's
+    if (l.D == 64)
+        hipLaunchKernelGGL((prefill_kernel<T, 64>), grid, dim3(kPrefillWaves * 64), 0, st, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<T, 128>), grid, dim3(kPrefillWaves * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+int launch_prefill(const PrefillLaunch &l, void *stream) {
+    if (l.S == 0 || l.max_q == 0 || l.total_rows == 0) return 0;
+    hipStream_t st = (hipStream_t)stream;
+    return (int)(l.dtype == 1 ? launch_prefill_t<_Float16>(l, st) : launch_prefill_t<__bf16>(l, st));
+}
+
 // ---------------------------------------------------------------- cache_write
 
 // One flat range of 16-byte vectors: token i's K rows, then its V rows, each

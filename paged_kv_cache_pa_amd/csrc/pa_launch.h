@@ -28,6 +28,22 @@ struct DecodeLaunch {
 // Returns 0 on success, else the hipError_t of the failed launch.
 int launch_decode(const DecodeLaunch &l, void *stream);
 
+// One prefill launch (multi-token queries), already validated; 16-bit only.
+struct PrefillLaunch {
+    const void *q, *k, *v;
+    const int32_t *tables, *lens, *qstart;
+    void *out;
+    float scale;
+    int32_t S, Hq, Hkv, D, dtype;
+    int32_t B, MBS, NB;
+    int32_t max_ctx;     // clamp for every context length
+    int32_t max_q;       // clamp for every chunk length; sizes the grid
+    int32_t total_rows;  // rows of q and out
+    int32_t layout;
+};
+
+int launch_prefill(const PrefillLaunch &l, void *stream);
+
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                        const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
                        int32_t hkv, int64_t row_bytes, int32_t layout, void *stream);

@@ -225,6 +225,51 @@ def test_multi_layer_copy_and_swap_checks(L):
     assert sw(good, good, 8, good, good, 64, 3, P(b.p.value + 2), 2, ctypes.byref(p), None) == ALIGN
 
 
+def pparams(**kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                max_blocks_per_seq=8, num_blocks=32, total_query_rows=40, max_query_len=32,
+                max_context_len=128, dtype=1, layout=1)
+    base.update(kw)
+    return pa.PrefillParams(*[base[f] for f, _ in pa.PrefillParams._fields_])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), DTYPE), (dict(dtype=0), UNSUP), (dict(head_dim=96), UNSUP),
+    (dict(num_q_heads=6, num_kv_heads=4), SHAPE), (dict(layout=3), SHAPE),
+    (dict(block_size=12), SHAPE), (dict(max_context_len=129), SHAPE),
+    (dict(max_query_len=200), SHAPE), (dict(num_seqs=-1), SHAPE),
+    (dict(total_query_rows=-1), SHAPE), (dict(max_blocks_per_seq=0), SHAPE),
+])
+def test_prefill_rejects_bad_params(L, kw, code):
+    b = Buf()
+    p = pparams(**kw)
+    assert L.pa_prefill(b.p, b.p, b.p, b.p, b.p, b.p, ctypes.c_float(1.0), b.p,
+                        ctypes.byref(p), None) == code
+
+
+def test_prefill_pointer_checks(L):
+    b = Buf()
+    p = pparams()
+    f = ctypes.c_float(1.0)
+    for i in range(7):
+        args = [b.p] * 7
+        args[i] = None
+        assert L.pa_prefill(*args[:6], f, args[6], ctypes.byref(p), None) == NULL
+    for i in (0, 1, 2, 6):
+        args = [b.p] * 7
+        args[i] = b.odd
+        assert L.pa_prefill(*args[:6], f, args[6], ctypes.byref(p), None) == ALIGN
+    odd4 = ctypes.c_void_p(b.p.value + 2)
+    for i in (3, 4, 5):
+        args = [b.p] * 7
+        args[i] = odd4
+        assert L.pa_prefill(*args[:6], f, args[6], ctypes.byref(p), None) == ALIGN
+    for kw in (dict(num_seqs=0), dict(total_query_rows=0), dict(max_query_len=0)):
+        assert L.pa_prefill(None, None, None, None, None, None, f, None,
+                            ctypes.byref(pparams(**kw)), None) == OK
+    assert L.pa_prefill(b.p, b.p, b.p, b.p, b.p, b.p, f, b.p, None, None) == NULL
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 
