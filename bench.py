@@ -339,6 +339,63 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+PREFILL_POINTS = (
+    # (label, dtype, seqs, context, chunk, Hq, Hkv)
+    ("OPT-13B prompt 8 x 1024", "f16", 8, 1024, 1024, 40, 40),
+    ("GQA chunk 512 after 3584 (4 seqs)", "bf16", 4, 4096, 512, 32, 8),
+)
+
+
+def prefill_flops(ctx, chunk, seqs, hq, d):
+    """Multiply-adds of the causal product, 2 flops each, for QK^T and PV:
+    each chunk row at position p sees p + 1 keys."""
+    pos = np.arange(ctx - chunk, ctx, dtype=np.int64)
+    return int(4 * d * hq * seqs * int((pos + 1).sum()))
+
+
+def prefill_rate(rounds=10, d=128):
+    """pa_prefill on the points above (head-major pools, block size 16):
+    median time per launch and achieved TFLOP/s against the dense 16-bit
+    matrix-core peak."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    res = {}
+    st = torch.cuda.current_stream()
+    g = torch.Generator(device="cuda").manual_seed(707)
+    for label, dt, S, ctx, chunk, hq, hkv in PREFILL_POINTS:
+        tdt = torch.float16 if dt == "f16" else torch.bfloat16
+        B = 16
+        nbs = ctx // B
+        nb = S * nbs
+        R = 2
+        pools = [(torch.randn((nb, hkv, B, d), generator=g, device="cuda").to(tdt),
+                  torch.randn((nb, hkv, B, d), generator=g, device="cuda").to(tdt))
+                 for _ in range(R)]
+        table = torch.from_numpy(np.random.default_rng(7).permutation(nb).reshape(S, nbs)
+                                 .astype(np.int32)).cuda()
+        cl = torch.full((S,), ctx, dtype=torch.int32, device="cuda")
+        qs = torch.arange(0, (S + 1) * chunk, chunk, dtype=torch.int32, device="cuda")
+        q = torch.randn((S * chunk, hq, d), generator=g, device="cuda").to(tdt)
+        out = torch.empty_like(q)
+
+        def f(i):
+            k, v = pools[i % R]
+            pa.pa_prefill(q, k, v, table, cl, qs, 1.0 / np.sqrt(d), out, max_query_len=chunk,
+                          max_context_len=ctx, layout="HND")
+
+        for i in range(2 * R):
+            f(i)
+        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        fl = prefill_flops(ctx, chunk, S, hq, d)
+        res[label] = {"us": round(t * 1e6, 1), "TFLOP_s": round(fl / t / 1e12, 1),
+                      "frac_of_2500": round(fl / t / 2.5e15, 4), "flops": fl}
+        del pools
+        torch.cuda.empty_cache()
+    return res
+
+
 BLOCK_SWEEP_SIZES = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 
 
@@ -709,6 +766,8 @@ def main():
                     help="skip the dense ratio, copy_blocks and CPU legs (for profiling runs)")
     ap.add_argument("--counters-run", action="store_true",
                     help="short run for rocprofv3 --pmc passes (decode launches + calibration copy)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time pa_prefill (chunked prompt attention) only; one JSON line")
     ap.add_argument("--block-sweep", action="store_true",
                     help="decode time against block size (1..256), in order / scattered / "
                          "contiguous, on a 16 x 4096-token GQA batch; one JSON line per point")
@@ -742,6 +801,9 @@ def main():
         return
     if args.block_sweep:
         block_sweep()
+        return
+    if args.prefill:
+        print(json.dumps(prefill_rate()), flush=True)
         return
     dev = torch.device("cuda:0")
     t_gen = time.time()
@@ -863,7 +925,7 @@ def main():
             result["copy_blocks"] = {"error": repr(e)}
         log("copy_blocks done")
         for key, fn in (("copy_blocks_layers", copy_layers_rate), ("swap", swap_rate),
-                        ("block_manager", block_manager_rate)):
+                        ("block_manager", block_manager_rate), ("prefill", prefill_rate)):
             try:
                 result[key] = fn()
             except Exception as e:
