@@ -187,6 +187,30 @@ def copy_blocks_rate(rounds=15):
             "replicas": R}
 
 
+def hbm_reference(rounds=10, gib=1):
+    """Reference rates of plain PyTorch kernels on the same GPU (not this
+    library): a device-to-device copy (bytes read + written) and a sum over
+    int64 words (bytes read), each over ``gib`` GiB, so the decode and copy
+    rates can be read against what a simple streaming kernel reaches here."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    n = (gib << 30) // 8
+    src = torch.randint(0, 1 << 20, (n,), dtype=torch.int64, device="cuda")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.int64, device="cuda")
+    res = {}
+    for name, fn, nbytes in (("copy_GB_s", lambda i: dst.copy_(src), 2 * n * 8),
+                             ("sum_read_GB_s", lambda i: torch.sum(src, out=acc), n * 8)):
+        fn(0)
+        t = float(np.median([time_group(fn, 1, st) for _ in range(rounds)]))
+        res[name] = round(nbytes / t / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    res["what"] = "torch copy_ / sum over 1 GiB of int64 on the same GPU"
+    return res
+
+
 def copy_layers_rate(rounds=10, layers=40):
     """pa_copy_blocks_layers: the 80 copy-on-write pairs of the
     parallel-sampling workload applied to every one of OPT-13B's 40 layers in
@@ -924,7 +948,8 @@ def main():
         except Exception as e:
             result["copy_blocks"] = {"error": repr(e)}
         log("copy_blocks done")
-        for key, fn in (("copy_blocks_layers", copy_layers_rate), ("swap", swap_rate),
+        for key, fn in (("hbm_reference", hbm_reference),
+                        ("copy_blocks_layers", copy_layers_rate), ("swap", swap_rate),
                         ("block_manager", block_manager_rate), ("prefill", prefill_rate)):
             try:
                 result[key] = fn()
