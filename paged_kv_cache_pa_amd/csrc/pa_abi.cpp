@@ -239,9 +239,10 @@ int pa_prefill(const void *q, const void *k_cache, const void *v_cache,
     if (p->max_query_len > p->max_context_len) return PA_ERR_SHAPE;
     if (p->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
     if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (p->num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
-    const int64_t tiles = ((int64_t)p->max_query_len + 63) / 64;
-    if ((int64_t)p->num_seqs * tiles > 0x7FFFFFFF / 256) return PA_ERR_UNSUPPORTED;
+    // grid (heads, sequences, row tiles): y and z are limited to 65535
+    if (p->num_seqs > 65535) return PA_ERR_UNSUPPORTED;
+    if (((int64_t)p->max_query_len + pa::kPrefillTileRows - 1) / pa::kPrefillTileRows > 65535)
+        return PA_ERR_UNSUPPORTED;
     if ((int64_t)p->total_query_rows * p->num_q_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     if (p->num_seqs == 0 || p->total_query_rows == 0 || p->max_query_len == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)

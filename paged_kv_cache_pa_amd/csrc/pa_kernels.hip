@@ -1101,17 +1101,25 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
 // are already in the pool); chunk row r sits at position n - T + r and
 // attends to positions 0 .. n - T + r.
 //
-// One workgroup of 4 waves per (sequence, 64-row tile of its chunk, query
-// head); each wave owns 16 query rows.  The workgroup walks the keys in
-// 16-token tiles: each thread loads one 16-byte piece of the next tile's K
-// and V rows into registers, the tile is written to one of two LDS buffers,
-// and every wave computes its 16 x 16 score tile on matrix cores as
+// One workgroup of 4 waves per (query head, sequence, 64-row tile of its
+// chunk); each wave owns kPrefillCols 16-row column tiles (one: a second
+// tile sharing each operand read measured no faster and halves the
+// occupancy).  The workgroup walks the keys in 32-token tiles: each thread
+// loads two 16-byte pieces of the next tile's K and V rows into registers,
+// the tile is written to one of two LDS buffers (one barrier per tile), and
+// for each 16-key sub-tile every wave computes its 16 x 16 score tile on
+// matrix cores as
 // S^T = K Q^T (K from LDS as the A operand, Q^T held in registers), updates
 // its running softmax per query column, and accumulates O^T += V^T P^T with
 // V^T read from LDS by the transposing ds_read_b64_tr_b16 (lane l addresses
 // row l / 4, columns d0 + 4 (l % 4), and receives V[4 (l / 16) + j][d0 + l %
 // 16], the A-operand layout) and P^T reused in place as the B operand.  The
-// causal mask and the chunk's end are applied per score.  fp16 and bf16.
+// causal mask and the chunk's end are applied per score.  The running max
+// of a query column moves only when a score exceeds it by more than 2^8
+// (weights then stay <= 256, exact in fp16 / bf16, and the final division
+// by the running sum is unchanged in exact arithmetic), so the accumulator
+// rescale -- 32 multiplies per lane on matrix-core results -- runs in a
+// rare wave-uniform branch instead of on every tile.  fp16 and bf16.
 struct PrefillArgs {
     const char *q, *k, *v;
     const int32_t *tables, *lens, *qstart;
@@ -1122,33 +1130,46 @@ struct PrefillArgs {
 };
 
 constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRows = 16 * kPrefillWaves;  // query rows per workgroup
+constexpr float kLazy = 8.0f;    // log2 of the largest weight before a rescale
+constexpr int kPrefillCols = 1;  // 16-row column tiles per wave
+constexpr int kPrefillSub = 2;   // 16-key sub-tiles per LDS tile (one barrier each)
+constexpr int kPrefillRows = 16 * kPrefillCols * kPrefillWaves;  // query rows per workgroup
+static_assert(kPrefillRows == kPrefillTileRows, "the host checks grid z with kPrefillTileRows");
 
 typedef short short4_t2 __attribute__((ext_vector_type(4)));
 
-template <typename T, int D>
+template <typename T, int D, int NQ, int KS>
 __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
     using E = Elem<T>;
     using M = Mma<T>;
     constexpr int KL = D / 32;           // 32-dim slices of the score product
     constexpr int DS = D / 16;           // 16-dim slices of the output
-    constexpr int ROW = D * 2 + 16;      // padded LDS row of a K or V tile (bytes)
-    constexpr int TILE = 16 * ROW;
+    // Padded LDS rows: a K row shifts 4 banks (16 lanes read 16 rows x 16 B),
+    // a V row 8 banks (32 lanes of the transposing read cover 8 rows x 32 B).
+    constexpr int KROW = D * 2 + 16, VROW = D * 2 + 32;
+    constexpr int KTILE = 16 * KROW, VTILE = 16 * VROW;
     constexpr int CPR = D * 2 / 16;      // 16-byte pieces per row
-    constexpr int LOADERS = 16 * CPR;    // threads that load one tile (<= 256)
-    static_assert(LOADERS <= kPrefillWaves * 64, "one piece per thread");
+    constexpr int KT = 16 * KS;          // keys per LDS tile (KS sub-tiles of 16)
+    constexpr int WROWS = 16 * NQ;       // query rows per wave
+    constexpr int GROWS = WROWS * kPrefillWaves;
+    constexpr int PIECES = KS * 16 * CPR;               // per tile, of K (and of V)
+    constexpr int PPT = PIECES / (kPrefillWaves * 64);  // per thread
+    static_assert(PPT >= 1 && PPT * kPrefillWaves * 64 == PIECES, "whole pieces per thread");
 
     __shared__ int32_t s_tab[kTableChunk];
-    __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILE];  // [buffer][K|V][tile]
+    __shared__ __attribute__((aligned(16))) char s_k[2][KS * KTILE];  // [buffer][keys]
+    __shared__ __attribute__((aligned(16))) char s_v[2][KS * VTILE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;  // key row of the A operand; query column of the scores
     const int kb = lane >> 4;   // k-block of the operands; 4-key group of the scores
-    const int s = blockIdx.x / a.tiles;
-    const int tile = blockIdx.x - s * a.tiles;
-    const int h = blockIdx.y;
+    // Grid (heads, sequences, tiles), dispatched x first: the last tiles of
+    // every chunk, which see the most keys, start first.
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int tile = a.tiles - 1 - (int)blockIdx.z;
     const int g = h / (a.Hq / a.Hkv);
 
     // The chunk's rows, clamped so that no access leaves q, out or the table.
@@ -1159,120 +1180,191 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
     int rows = q1 - q0;  // chunk length
     rows = rows > a.max_q ? a.max_q : rows;
     rows = rows > n ? n : rows;
-    const int tr0 = tile * kPrefillRows;
+    const int tr0 = tile * GROWS;
     if (tr0 >= rows) return;  // the whole workgroup idles
-    const int r0 = tr0 + 16 * wave;
-    const int rows_w = rows - r0 < 0 ? 0 : (rows - r0 > 16 ? 16 : rows - r0);
-    const int my_pos = n - rows + r0 + col;                       // this lane's query position
+    const int r0 = tr0 + WROWS * wave;                         // this wave's first row
+    const int rows_w = rows - r0 < 0 ? 0 : (rows - r0 > WROWS ? WROWS : rows - r0);
     const int w_last = rows_w ? n - rows + r0 + rows_w - 1 : -1;  // last key of this wave
-    const int nkeys = n - rows + (tr0 + kPrefillRows < rows ? tr0 + kPrefillRows : rows);  // of the WG
+    const int nkeys = n - rows + (tr0 + GROWS < rows ? tr0 + GROWS : rows);  // of the WG
 
-    // B operand of S^T = K Q^T: query row r0 + col, dims 32 i + 8 kb .. + 7.
-    const int64_t qrow = (int64_t)(q0 + r0 + col) * a.Hq + h;
-    vec4 qb[KL];
+    // Column tile c holds rows r0 + 16 c + col.  B operand of S^T = K Q^T:
+    // that row's dims 32 i + 8 kb .. + 7 (zero past the chunk).
+    vec4 qb[NQ][KL];
+    int my_pos[NQ];
 #pragma unroll
-    for (int i = 0; i < KL; ++i)
-        qb[i] = col < rows_w ? load_cached(a.q + (qrow * D + 32 * i + 8 * kb) * 2)
-                             : vec4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < NQ; ++c) {
+        const int r = r0 + 16 * c + col;
+        my_pos[c] = n - rows + r;
+        const int64_t qrow = (int64_t)(q0 + r) * a.Hq + h;
+#pragma unroll
+        for (int i = 0; i < KL; ++i)
+            qb[c][i] = r < rows ? load_cached(a.q + (qrow * D + 32 * i + 8 * kb) * 2)
+                                : vec4{0u, 0u, 0u, 0u};
+    }
 
-    float m = kNegBig, lsum = 0.0f;
-    float4_t acc[DS];
+    float m[NQ], lsum[NQ];
+    float4_t acc[NQ][DS];
 #pragma unroll
-    for (int d = 0; d < DS; ++d) acc[d] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NQ; ++c) {
+        m[c] = kNegBig;
+        lsum[c] = 0.0f;
+#pragma unroll
+        for (int d = 0; d < DS; ++d) acc[c][d] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int B = 1 << a.log2B;
     const int32_t *trow = a.tables + (int64_t)s * a.MBS;
     const int64_t head0 = (int64_t)g * a.head_bytes;
-    const int lkey = tid / CPR, lpiece = tid % CPR;  // this thread's piece of a tile
-    const bool loader = tid < LOADERS;
     const int nblk = (nkeys + B - 1) >> a.log2B;
 
+    // The KS * 16 rows of a tile are PIECES 16-byte pieces of K (and as many
+    // of V); thread tid moves pieces tid, tid + 256, ...
+    struct Regs {
+        vec4 k[PPT], v[PPT];
+    };
     for (int cb = 0; cb < nblk; cb += kTableChunk) {
         const int cn = nblk - cb < kTableChunk ? nblk - cb : kTableChunk;
         const int ck0 = cb << a.log2B;
         const int ck1 = (cb + cn) << a.log2B < nkeys ? (cb + cn) << a.log2B : nkeys;
-        const int nst = (ck1 - ck0 + 15) >> 4;
+        const int nst = (ck1 - ck0 + KT - 1) / KT;
         __syncthreads();  // the previous chunk's readers are done
         stage_table(trow, cb, cn, a.NB, s_tab, tid, blockDim.x);
         __syncthreads();
 
-        vec4 kr, vr;
-        auto fetch = [&](int j) {  // this thread's piece of tile j (clamped to a real key)
-            int t = ck0 + 16 * j + lkey;
-            t = t < ck1 ? t : ck1 - 1;
-            const int64_t row = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
-                                (int64_t)(t & (B - 1)) * a.tok_bytes + head0 + lpiece * 16;
-            kr = load_cached(a.k + row);
-            vr = load_cached(a.v + row);
+        // Loads of tile j (keys clamped to the chunk, so tiles past the end
+        // reload its last key: every fetch is unconditional and each wait
+        // names exactly the set it needs).
+        auto fetch = [&](Regs &r, int j) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int pc = tid + i * kPrefillWaves * 64;
+                int t = ck0 + KT * j + pc / CPR;
+                t = t < ck1 ? t : ck1 - 1;
+                const int64_t row = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
+                                    (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
+                                    (pc % CPR) * 16;
+                r.k[i] = load_cached(a.k + row);
+                r.v[i] = load_cached(a.v + row);
+            }
         };
-        auto stash = [&](int buf) {
-            *reinterpret_cast<vec4 *>(&s_kv[buf][0][lkey * ROW + lpiece * 16]) = kr;
-            *reinterpret_cast<vec4 *>(&s_kv[buf][1][lkey * ROW + lpiece * 16]) = vr;
+        auto stash = [&](const Regs &r, int buf) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int pc = tid + i * kPrefillWaves * 64;
+                const int key = pc / CPR;  // 0 .. KT - 1
+                const int sub = key >> 4, row = key & 15, off = (pc % CPR) * 16;
+                *reinterpret_cast<vec4 *>(&s_k[buf][sub * KTILE + row * KROW + off]) = r.k[i];
+                *reinterpret_cast<vec4 *>(&s_v[buf][sub * VTILE + row * VROW + off]) = r.v[i];
+            }
         };
-        if (loader) {
-            fetch(0);
-            stash(0);
-        }
-        __syncthreads();
-        for (int j = 0; j < nst; ++j) {
-            const int buf = j & 1;
-            if (loader && j + 1 < nst) fetch(j + 1);  // in flight during this tile's math
-            const int key0 = ck0 + 16 * j;
-            if (key0 <= w_last) {  // wave-uniform: tiles past this wave's rows are skipped
-                const char *kt = s_kv[buf][0];
-                const char *vt = s_kv[buf][1];
-                float4_t sc = {0.f, 0.f, 0.f, 0.f};
+        auto compute = [&](int buf, int j) {
 #pragma unroll
-                for (int i = 0; i < KL; ++i) {
-                    const vec4 ka = *reinterpret_cast<const vec4 *>(kt + col * ROW + (32 * i + 8 * kb) * 2);
-                    sc = M::qk(ka, qb[i], sc);
+            for (int u = 0; u < KS; ++u) {
+                const int key0 = ck0 + KT * j + 16 * u;
+                if (key0 > w_last) break;  // wave-uniform: keys past this wave's rows
+                const char *kt = s_k[buf] + u * KTILE;
+                const char *vt = s_v[buf] + u * VTILE;
+                vec4 ka[KL];
+#pragma unroll
+                for (int i = 0; i < KL; ++i)
+                    ka[i] = *reinterpret_cast<const vec4 *>(kt + col * KROW + (32 * i + 8 * kb) * 2);
+                // Scores of this sub-tile; the running max m is moved only when a
+                // score exceeds it by more than 2^kLazy (weights then stay <=
+                // 2^kLazy, exact in fp16 and bf16), so the accumulators are
+                // rescaled rarely, in a wave-uniform branch.
+                float x[NQ][4];
+                bool grow = false;
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    float4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < KL; ++i) sc = M::qk(ka[i], qb[c][i], sc);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int key = key0 + 4 * kb + jj;
+                        x[c][jj] = (key > my_pos[c] || key >= ck1) ? -__builtin_inff()
+                                                                   : sc[jj] * a.qk_scale;
+                    }
+                    float mx = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
+                    grow |= mx > m[c] + kLazy;
                 }
-                float x[4];
+                if (__any(grow)) {
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int key = key0 + 4 * kb + jj;
-                    x[jj] = (key > my_pos || key >= ck1) ? -__builtin_inff() : sc[jj] * a.qk_scale;
+                    for (int c = 0; c < NQ; ++c) {
+                        float mx = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
+                        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                        const float mn = fmaxf(m[c], mx);
+                        const float alpha = fexp2(m[c] - mn);
+                        m[c] = mn;
+                        lsum[c] *= alpha;
+#pragma unroll
+                        for (int d = 0; d < DS; ++d) acc[c][d] = acc[c][d] * alpha;
+                    }
                 }
-                float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                const float mn = fmaxf(m, mx);
-                const float alpha = fexp2(m - mn);
-                float p[4];
+                vec2 pb[NQ], pr[NQ];
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[jj] - mn);
-                lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-                m = mn;
-                const vec2 pb = M::pack(p[0], p[1], p[2], p[3]);
-                const vec2 pr = M::rest(p[0], p[1], p[2], p[3], pb);
+                for (int c = 0; c < NQ; ++c) {
+                    float p[4];
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[c][jj] - m[c]);
+                    lsum[c] += (p[0] + p[1]) + (p[2] + p[3]);
+                    pb[c] = M::pack(p[0], p[1], p[2], p[3]);
+                    pr[c] = M::rest(p[0], p[1], p[2], p[3], pb[c]);
+                }
 #pragma unroll
                 for (int d = 0; d < DS; ++d) {
                     // A operand of O^T += V^T P^T through the transposing read
-                    const char *src = vt + (lane >> 2) * ROW + (16 * d + 4 * (lane & 3)) * 2;
+                    const char *src = vt + (lane >> 2) * VROW + (16 * d + 4 * (lane & 3)) * 2;
                     const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (short4_t2 __attribute__((address_space(3))) *)(src));
                     const vec2 va = __builtin_bit_cast(vec2, t4);
-                    acc[d] = acc[d] * alpha;
-                    acc[d] = M::pv(va, pb, acc[d]);
-                    if constexpr (M::kSplit) acc[d] = M::pv(va, pr, acc[d]);
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c) {
+                        acc[c][d] = M::pv(va, pb[c], acc[c][d]);
+                        if constexpr (M::kSplit) acc[c][d] = M::pv(va, pr[c], acc[c][d]);
+                    }
                 }
             }
-            if (loader && j + 1 < nst) stash(buf ^ 1);
+        };
+        // Two register sets: tile j + 1 is in flight while tile j is
+        // computed, and tile j + 2 is requested before it; a tile is written
+        // to LDS one compute period after its loads were issued.
+        Regs r0, r1;
+        fetch(r0, 0);
+        fetch(r1, 1);
+        stash(r0, 0);
+        __syncthreads();
+        for (int j = 0; j < nst; j += 2) {
+            fetch(r0, j + 2);
+            compute(0, j);
+            stash(r1, 1);
             __syncthreads();  // tile j + 1 is in place; tile j's readers are done
+            if (j + 1 >= nst) break;
+            fetch(r1, j + 3);
+            compute(1, j + 1);
+            stash(r0, 0);
+            __syncthreads();
         }
     }
 
     // The four lanes of a query column (col, col + 16, col + 32, col + 48)
     // hold the same running max and partial sums over their keys.
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    if (col < rows_w) {
-        const float inv = 1.0f / lsum;
-        const int64_t o = qrow * D;
 #pragma unroll
-        for (int d = 0; d < DS; ++d)
+    for (int c = 0; c < NQ; ++c) {
+        float l = lsum[c];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const int r = r0 + 16 * c + col;
+        if (r < rows) {
+            const float inv = 1.0f / l;
+            const int64_t o = ((int64_t)(q0 + r) * a.Hq + h) * D;
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) E::store(a.out, o + 16 * d + 4 * kb + jj, acc[d][jj] * inv);
+            for (int d = 0; d < DS; ++d)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    E::store(a.out, o + 16 * d + 4 * kb + jj, acc[c][d][jj] * inv);
+        }
     }
 }
 
@@ -1308,12 +1400,14 @@ static hipError_t launch_prefill_t(const PrefillLaunch &l, hipStream_t st) {
         a.head_bytes = row * l.B;
     }
     a.blk_bytes = row * l.Hkv * l.B;
-    const dim3 grid((unsigned)((int64_t)l.S * a.tiles), (unsigned)l.Hq);
+    const dim3 grid((unsigned)l.Hq, (unsigned)l.S, (unsigned)a.tiles);
     (void)hipGetLastError();  // an error left by other code is not this launch's
     if (l.D == 64)
-        hipLaunchKernelGGL((prefill_kernel<T, 64>), grid, dim3(kPrefillWaves * 64), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<T, 64, kPrefillCols, kPrefillSub>), grid, dim3(kPrefillWaves * 64), 0,
+                           st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, 128>), grid, dim3(kPrefillWaves * 64), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<T, 128, kPrefillCols, kPrefillSub>), grid, dim3(kPrefillWaves * 64),
+                           0, st, a);
     return hipGetLastError();
 }
 

@@ -42,6 +42,10 @@ struct PrefillLaunch {
     int32_t layout;
 };
 
+// Query rows of a chunk one prefill workgroup covers (grid z = ceil(max_q /
+// kPrefillTileRows), at most 65535).
+constexpr int kPrefillTileRows = 64;
+
 int launch_prefill(const PrefillLaunch &l, void *stream);
 
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
