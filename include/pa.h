@@ -253,7 +253,7 @@ int pa_swap_blocks(void *const *dst_k, void *const *dst_v, int32_t dst_num_block
  * query_start[num_seqs] = total_query_rows.  Device pointers.
  * Host-checked: dtype fp16 or bf16 (fp32: PA_ERR_UNSUPPORTED), head_dim 64
  * or 128 (else PA_ERR_UNSUPPORTED), num_seqs <= 65535 and max_query_len <=
- * 65535 * 64 (else PA_ERR_UNSUPPORTED), Hq a multiple of Hkv, block_size a
+ * 65535 * 128 (else PA_ERR_UNSUPPORTED), Hq a multiple of Hkv, block_size a
  * power of two in [1, 256],
  * max_context_len <= max_blocks_per_seq * block_size, 16-byte aligned q,
  * caches and out, 4-byte aligned int arrays.

@@ -1101,13 +1101,13 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
 // are already in the pool); chunk row r sits at position n - T + r and
 // attends to positions 0 .. n - T + r.
 //
-// One workgroup of 4 waves per (query head, sequence, 64-row tile of its
-// chunk); each wave owns kPrefillCols 16-row column tiles (one: a second
-// tile sharing each operand read measured no faster and halves the
-// occupancy).  The workgroup walks the keys in 32-token tiles: each thread
-// loads two 16-byte pieces of the next tile's K and V rows into registers,
-// the tile is written to one of two LDS buffers (one barrier per tile), and
-// for each 16-key sub-tile every wave computes its 16 x 16 score tile on
+// One workgroup of 4 waves per (query head, sequence, 128-row tile of its
+// chunk); each wave owns two 16-row column tiles, which share every K and
+// V^T operand it reads from LDS.  The workgroup walks the keys in tiles of 16
+// (head dim 128) or 32 (head dim 64) tokens: each thread loads one 16-byte
+// piece of K and one of V per 16 keys, two tiles ahead of the one being
+// computed, the tile is written to one of two LDS buffers (one barrier per
+// tile), and for each 16-key sub-tile every wave computes its score tiles on
 // matrix cores as
 // S^T = K Q^T (K from LDS as the A operand, Q^T held in registers), updates
 // its running softmax per query column, and accumulates O^T += V^T P^T with
@@ -1131,8 +1131,10 @@ struct PrefillArgs {
 
 constexpr int kPrefillWaves = 4;
 constexpr float kLazy = 8.0f;    // log2 of the largest weight before a rescale
-constexpr int kPrefillCols = 1;  // 16-row column tiles per wave
-constexpr int kPrefillSub = 2;   // 16-key sub-tiles per LDS tile (one barrier each)
+constexpr int kPrefillCols = 2;  // 16-row column tiles per wave
+// 16-key sub-tiles per LDS tile (one barrier per tile): as few as give every
+// thread a whole 16-byte piece of K and of V to load
+constexpr int prefill_sub(int D) { return D == 64 ? 2 : 1; }
 constexpr int kPrefillRows = 16 * kPrefillCols * kPrefillWaves;  // query rows per workgroup
 static_assert(kPrefillRows == kPrefillTileRows, "the host checks grid z with kPrefillTileRows");
 
@@ -1264,10 +1266,22 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                 if (key0 > w_last) break;  // wave-uniform: keys past this wave's rows
                 const char *kt = s_k[buf] + u * KTILE;
                 const char *vt = s_v[buf] + u * VTILE;
+                // Both operands of the sub-tile are requested from LDS before
+                // any math, so the V^T reads overlap the score product and the
+                // softmax instead of waiting behind them.
                 vec4 ka[KL];
 #pragma unroll
                 for (int i = 0; i < KL; ++i)
                     ka[i] = *reinterpret_cast<const vec4 *>(kt + col * KROW + (32 * i + 8 * kb) * 2);
+                vec2 va[DS];
+#pragma unroll
+                for (int d = 0; d < DS; ++d) {
+                    // A operand of O^T += V^T P^T through the transposing read
+                    const char *src = vt + (lane >> 2) * VROW + (16 * d + 4 * (lane & 3)) * 2;
+                    const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (short4_t2 __attribute__((address_space(3))) *)(src));
+                    va[d] = __builtin_bit_cast(vec2, t4);
+                }
                 // Scores of this sub-tile; the running max m is moved only when a
                 // score exceeds it by more than 2^kLazy (weights then stay <=
                 // 2^kLazy, exact in fp16 and bf16), so the accumulators are
@@ -1279,12 +1293,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                     float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < KL; ++i) sc = M::qk(ka[i], qb[c][i], sc);
+                    // keys key0 + 4 kb + jj with jj > lim are hidden (causal, or
+                    // past the chunk's end)
+                    const int lim = min(my_pos[c], ck1 - 1) - (key0 + 4 * kb);
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int key = key0 + 4 * kb + jj;
-                        x[c][jj] = (key > my_pos[c] || key >= ck1) ? -__builtin_inff()
-                                                                   : sc[jj] * a.qk_scale;
-                    }
+                    for (int jj = 0; jj < 4; ++jj)
+                        x[c][jj] = jj > lim ? -__builtin_inff() : sc[jj] * a.qk_scale;
                     float mx = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
                     grow |= mx > m[c] + kLazy;
                 }
@@ -1314,15 +1328,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                 }
 #pragma unroll
                 for (int d = 0; d < DS; ++d) {
-                    // A operand of O^T += V^T P^T through the transposing read
-                    const char *src = vt + (lane >> 2) * VROW + (16 * d + 4 * (lane & 3)) * 2;
-                    const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (short4_t2 __attribute__((address_space(3))) *)(src));
-                    const vec2 va = __builtin_bit_cast(vec2, t4);
 #pragma unroll
                     for (int c = 0; c < NQ; ++c) {
-                        acc[c][d] = M::pv(va, pb[c], acc[c][d]);
-                        if constexpr (M::kSplit) acc[c][d] = M::pv(va, pr[c], acc[c][d]);
+                        acc[c][d] = M::pv(va[d], pb[c], acc[c][d]);
+                        if constexpr (M::kSplit) acc[c][d] = M::pv(va[d], pr[c], acc[c][d]);
                     }
                 }
             }
@@ -1403,10 +1412,10 @@ static hipError_t launch_prefill_t(const PrefillLaunch &l, hipStream_t st) {
     const dim3 grid((unsigned)l.Hq, (unsigned)l.S, (unsigned)a.tiles);
     (void)hipGetLastError();  // an error left by other code is not this launch's
     if (l.D == 64)
-        hipLaunchKernelGGL((prefill_kernel<T, 64, kPrefillCols, kPrefillSub>), grid, dim3(kPrefillWaves * 64), 0,
+        hipLaunchKernelGGL((prefill_kernel<T, 64, kPrefillCols, prefill_sub(64)>), grid, dim3(kPrefillWaves * 64), 0,
                            st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, 128, kPrefillCols, kPrefillSub>), grid, dim3(kPrefillWaves * 64),
+        hipLaunchKernelGGL((prefill_kernel<T, 128, kPrefillCols, prefill_sub(128)>), grid, dim3(kPrefillWaves * 64),
                            0, st, a);
     return hipGetLastError();
 }

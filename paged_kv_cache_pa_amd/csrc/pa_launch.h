@@ -44,7 +44,7 @@ struct PrefillLaunch {
 
 // Query rows of a chunk one prefill workgroup covers (grid z = ceil(max_q /
 // kPrefillTileRows), at most 65535).
-constexpr int kPrefillTileRows = 64;
+constexpr int kPrefillTileRows = 128;
 
 int launch_prefill(const PrefillLaunch &l, void *stream);
 
