@@ -1,9 +1,11 @@
 """Benchmark: paged decode attention at the OPT-13B layer shape on one MI355X.
 
-One step = the decode iteration's hot path over one batch: pa_cache_write
-of each sequence's newest token into its slot, then pa_decode over the whole
-batch (64 sequences, 40/40 heads, head_dim 128, fp16, 16-token blocks,
-lognormal context lengths, blocks scattered by a seeded permutation).  The
+One step = the decode iteration's hot path over one batch, in one launch
+(pa_decode_append): each sequence's newest token is stored in its slot and
+the whole batch attends (64 sequences, 40/40 heads, head_dim 128, fp16,
+16-token blocks, lognormal context lengths, blocks scattered by a seeded
+permutation).  The same step as two launches (pa_cache_write, then
+pa_decode) is timed too and reported beside it.  The
 batch's copy-on-write list is empty at this shape (no forks), so no
 copy_blocks launch is part of the step; copy_blocks is timed on its own on
 the parallel-sampling workload and reported beside the step.
@@ -201,7 +203,7 @@ def hbm_reference(rounds=10, gib=1):
     acc = torch.empty((), dtype=torch.int64, device="cuda")
     res = {}
     for name, fn, nbytes in (("copy_GB_s", lambda i: dst.copy_(src), 2 * n * 8),
-                             ("sum_read_GB_s", lambda i: torch.sum(src, out=acc), n * 8)):
+                             ("sum_read_GB_s", lambda i: torch.sum(src, dim=0, out=acc), n * 8)):
         fn(0)
         t = float(np.median([time_group(fn, 1, st) for _ in range(rounds)]))
         res[name] = round(nbytes / t / 1e9, 1)
@@ -652,9 +654,12 @@ def counters_run(args):
     out = torch.empty_like(q)
     bt = torch.from_numpy(p.block_tables).to(dev)
     cl = torch.from_numpy(p.context_lens).to(dev)
+    rng = np.random.default_rng(2020)
+    k_new = torch.from_numpy(W.randn(rng, (S, Hkv, D), "f16")).to(dev)
+    v_new = torch.from_numpy(W.randn(rng, (S, Hkv, D), "f16")).to(dev)
     for _ in range(args.steps):
-        pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=int(p.context_lens.max()),
-                     layout=lay)
+        pa.pa_decode_append(q, k_new, v_new, k, v, bt, cl, p.scale, out,
+                            max_context_len=int(p.context_lens.max()), layout=lay)
     torch.cuda.synchronize()
     nbc = 4096  # calibration pool: 4096 blocks of 160 KiB per tensor
     kc = torch.zeros((nbc, 16, 40, 128), dtype=torch.float16, device=dev)
@@ -666,7 +671,8 @@ def counters_run(args):
     torch.cuda.synchronize()
     blk = 16 * 40 * 128 * 2
     print(json.dumps({"decode_launches": args.steps,
-                      "decode_algorithmic_bytes": decode_bytes(p.context_lens, Hq, Hkv, D, 2, B),
+                      "decode_algorithmic_bytes": decode_bytes(p.context_lens, Hq, Hkv, D, 2, B)
+                      + 2 * S * Hkv * D * 2,
                       "copy_launches": 3, "copy_read_bytes": 2 * half * blk,
                       "copy_write_bytes": 2 * half * blk, "kernel_sha256_16": kernel_hash()}),
           flush=True)
@@ -739,7 +745,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, commands):
     os.makedirs(out_dir, exist_ok=True)
     with open(os.path.join(out_dir, "decode_opt13b_f16_counters.json"), "w") as f:
         json.dump(counters, f, indent=1)
-    lines = ["# Kernel trace: OPT-13B-shape decode step (fp16, head-major pool)", "",
+    lines = ["# Kernel trace: OPT-13B-shape decode step (fp16, head-major pool; "
+             "pa_decode_append: newest token stored, then attention, one launch)", "",
              "Command (from the repository root, on one MI355X):", "", "```",
              commands[0], "```", "",
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
@@ -751,7 +758,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, commands):
                      f"{float(r['Percentage']):.1f}% |")
     dec = [r for r in stats if r["Name"].startswith(DECODE_KERNEL_PREFIX)][0]
     avg = float(dec["AverageNs"]) * 1e-9
-    lines += ["", f"Decode kernel: {meta['decode_algorithmic_bytes']} algorithmic bytes per launch / "
+    lines += ["", "Algorithmic bytes = K/V rows read + queries read + outputs written + the "
+              "newest K/V rows read and stored.",
+              "", f"Decode kernel: {meta['decode_algorithmic_bytes']} algorithmic bytes per launch / "
               f"{avg * 1e6:.2f} us = {meta['decode_algorithmic_bytes'] / avg / 1e9:.0f} GB/s "
               f"({meta['decode_algorithmic_bytes'] / avg / 8e12 * 100:.1f}% of 8 TB/s).",
               f"HBM traffic per launch from the counter passes: {hbm / 1e6:.1f} MB "
@@ -861,29 +870,41 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run(first, count, timed):
-        """Steps first .. first+count-1 in groups of R batches: each group
-        writes every batch's new token, then decodes the R batches back to
-        back (batch b of a group uses pool replica b), so the decode launches
-        of a group can be timed together with one event pair."""
+        """Steps first .. first+count-1 in groups of R batches; a step is one
+        pa_decode_append launch (the new token of every sequence written to
+        its slot, then attention over the batch); batch b of a group uses
+        pool replica b, and the launches of a group are timed together with
+        one event pair."""
         spans = []
         i = first
         while i < first + count:
             g = min(R, first + count - i)
-            for b in range(g):
-                k, v = pools[b]
-                pa.pa_cache_write(k_new, v_new, k, v, slots, layout=args.layout)
             if timed:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             for b in range(g):
                 k, v = pools[b]
-                pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl,
-                             partition_size=args.partition, workspace=ws, layout=args.layout)
+                pa.pa_decode_append(q, k_new, v_new, k, v, bt, cl, p.scale, out,
+                                    max_context_len=mcl, partition_size=args.partition,
+                                    workspace=ws, layout=args.layout)
             if timed:
                 e1.record(stream)
                 spans.append((e0, e1, g))
             i += g
         return spans
+
+    def run_two_launch(count):
+        """The same step as two launches (pa_cache_write, then pa_decode):
+        wall seconds per step."""
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(count):
+            k, v = pools[i % R]
+            pa.pa_cache_write(k_new, v_new, k, v, slots, layout=args.layout)
+            pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl,
+                         partition_size=args.partition, workspace=ws, layout=args.layout)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / count
 
     run(0, args.warmup, False)
     torch.cuda.synchronize()
@@ -896,10 +917,14 @@ def main():
     dec_avg = dec_total / args.steps
     log(f"timed {args.steps} steps: {wall / args.steps * 1e3:.4f} ms/step, "
         f"decode avg {dec_avg * 1e6:.2f} us per launch")
+    # (left out of --no-extras runs, so that a kernel trace of one holds only
+    # the fused launches)
+    two_launch = None if args.no_extras else run_two_launch(max(args.steps, 10))
 
     toks = int(lens.sum())
     value = toks * args.steps / wall
-    launch_bytes = decode_bytes(lens, Hq, Hkv, D, 2, B)
+    # attention's reads plus the newest rows written into their slots
+    launch_bytes = decode_bytes(lens, Hq, Hkv, D, 2, B) + 2 * S * Hkv * D * 2
     achieved = launch_bytes / dec_avg / 1e9
     traffic = traffic_from_counters(launch_bytes)
     result = {
@@ -916,8 +941,8 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
         "config": {
-            "workload": "OPT-13B-shape single-layer decode step (cache_write of each sequence's "
-                        "new token + paged decode), fp16",
+            "workload": "OPT-13B-shape single-layer decode step (each sequence's new token "
+                        "written to its slot + paged decode, one launch), fp16",
             "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "block_size": B, "sum_context_lens": toks, "max_context_len": mcl,
             "num_blocks": NB, "partition_size": args.partition, "kv_pool_replicas": R,
@@ -936,6 +961,7 @@ def main():
             "avg_launch_us": round(dec_avg * 1e6, 3),
             "timing": "HIP events around groups of back-to-back decode launches on the launch stream",
         },
+        "two_launch_ms_per_step": None if two_launch is None else round(two_launch * 1e3, 5),
     }
     if not args.no_extras:
         try:

@@ -155,6 +155,29 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               void *stream);
 
 /*
+ * decode_append: the decode iteration's write and attention in one launch.
+ * For every sequence s with n = context_lens[s] >= 1 the newest token's rows
+ * k_new[s], v_new[s] ([num_seqs, num_kv_heads, head_dim], the token at
+ * position n - 1) are written to that position's slot -- block
+ * block_tables[s][(n - 1) / B], offset (n - 1) % B, what pa_cache_write
+ * does with that slot ([Kwon] §3.4 "Kernel-Level Optimizations", item 1) --
+ * and out is what pa_decode computes over the n tokens afterwards.  The
+ * attention takes position n - 1 from k_new / v_new, so no workgroup waits
+ * for the write.  Pool contents are bit for bit those of pa_cache_write
+ * followed by pa_decode; out is too on the matrix-core path (grouped query
+ * heads, 16-bit types), while the other path adds position n - 1 as a last
+ * online-softmax step and may differ from pa_decode in rounding order only
+ * (deterministic, within pa_decode's tolerance).  Same parameters, layouts, checks,
+ * workspace and preconditions as pa_decode; k_new, v_new: device pointers,
+ * 16-byte aligned.  The newest slot must belong to sequence s alone (a
+ * shared last block is copied first: pa_copy_blocks).
+ */
+int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, void *out, const pa_decode_params *p, void *workspace,
+                     size_t ws_bytes, void *stream);
+
+/*
  * The same attention over a contiguous cache: token t of sequence s is row
  * (s, t) of k, v ([Res] "Attention over scattered blocks": the contiguous
  * cache addressed directly, no table).  Built from the same kernel source as

@@ -7,7 +7,7 @@ runs in the library's HIP kernels.  There is no CPU fallback: if the library
 is not built, every call raises.
 
 Entry points (same names as the C ABI):
-  pa_decode, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
+  pa_decode, pa_decode_append, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
   pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
 and the host block manager (``include/pa_block_manager.h``) as the class
 ``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
@@ -19,7 +19,7 @@ import os
 
 from .build import LIB_PATH
 
-__all__ = ["pa_decode", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
+__all__ = ["pa_decode", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
            "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill", "PaError",
            "lib",
            "LIB_PATH", "STATUS"]
@@ -95,6 +95,7 @@ def lib():
         DP, CP = ctypes.POINTER(DecodeParams), ctypes.POINTER(CacheParams)
         L.pa_decode_workspace_size.argtypes = [DP, ctypes.POINTER(SZ)]
         L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
+        L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
         L.pa_decode_dense.argtypes = [P, P, P, P, ctypes.c_float, P, DP, I32, P, SZ, P]
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I32, CP, P]
@@ -102,7 +103,8 @@ def lib():
         L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                  ctypes.POINTER(PrefillParams), P]
         L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
-        for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_dense", "pa_cache_write",
+        for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_append", "pa_decode_dense",
+                  "pa_cache_write",
                   "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
@@ -216,6 +218,37 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
     _check(lib().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
                            _ptr(ws), nbytes, _stream(stream)), "pa_decode")
+    return out
+
+
+def pa_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out,
+                     *, max_context_len=None, partition_size=0, workspace=None, stream=None,
+                     layout="NHD"):
+    """Write each sequence's newest token (k_new, v_new [S, Hkv, D], position
+    context_lens[s] - 1) into its slot and attend, in one launch; the same
+    result and pool contents as pa_cache_write followed by pa_decode."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k_new, "k_new", 3, q.dtype)
+    _need(v_new, "v_new", 3, q.dtype)
+    _need(k_cache, "k_cache", 4, q.dtype)
+    _need(v_cache, "v_cache", 4, q.dtype)
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v_cache.shape != k_cache.shape or out.shape != q.shape or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch between k_cache/v_cache, q/out or k_new/v_new")
+    if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout)
+    if tuple(k_new.shape) != (q.shape[0], p.num_kv_heads, p.head_dim):
+        raise ValueError("k_new / v_new must be [S, Hkv, D]")
+    ws, nbytes = _workspace(p, workspace, q.device)
+    _check(lib().pa_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                  float(scale), _ptr(out), ctypes.byref(p), _ptr(ws), nbytes,
+                                  _stream(stream)), "pa_decode_append")
     return out
 
 

@@ -80,7 +80,8 @@ size_t workspace_bytes(const pa_decode_params *p) {
 
 int run_decode(const void *q, const void *k, const void *v, const int32_t *tables,
                const int32_t *lens, float scale, void *out, const pa_decode_params *p,
-               void *ws, size_t ws_bytes, void *stream, bool dense, int32_t max_seq_len) {
+               void *ws, size_t ws_bytes, void *stream, bool dense, int32_t max_seq_len,
+               const void *k_new = nullptr, const void *v_new = nullptr) {
     if (p->num_seqs == 0) return PA_OK;
     if (!q || !k || !v || !lens || !out || (!dense && !tables)) return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGN;
@@ -113,6 +114,12 @@ int run_decode(const void *q, const void *k, const void *v, const int32_t *table
     l.pos_stride = dense ? max_seq_len : 0;
     l.layout = p->layout;
     l.dense = dense;
+    if (k_new) {  // append mode: the pools are written too
+        l.k_new = k_new;
+        l.v_new = v_new;
+        l.k_w = const_cast<void *>(k);
+        l.v_w = const_cast<void *>(v);
+    }
     const int e = pa::launch_decode(l, stream);
     return hip_status(e);
 }
@@ -191,6 +198,19 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
     if (st != PA_OK) return st;
     return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
                       ws_bytes, stream, false, 0);
+}
+
+int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                     void *v_cache, const int32_t *block_tables, const int32_t *context_lens,
+                     float scale, void *out, const pa_decode_params *p, void *workspace,
+                     size_t ws_bytes, void *stream) {
+    const int st = check_paged_shape(p);
+    if (st != PA_OK) return st;
+    if (p->num_seqs == 0) return PA_OK;
+    if (!k_new || !v_new) return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ALIGN;
+    return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
+                      ws_bytes, stream, false, 0, k_new, v_new);
 }
 
 int pa_decode_dense(const void *q, const void *k, const void *v, const int32_t *context_lens,

@@ -190,6 +190,13 @@ struct DecodeArgs {
     float *ws_acc;   // [S, Hq, P, D]
     float *ws_ml;    // [S, Hq, P, 2]
     float qk_scale;  // scale * log2(e)
+    // Append mode (k_new != nullptr): the newest token of each sequence,
+    // rows [S, Hkv, D], is read from here for position n - 1 and written to
+    // its slot through k_w / v_w (the same pools as k / v).
+    const char *k_new;
+    const char *v_new;
+    char *k_w;
+    char *v_w;
     int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, PS, P;
     int32_t rank;       // 1: longest-first sequence order (S <= kRankMaxSeqs)
     int32_t spec_blocks;  // table entries a partition can need (fetched before its length)
@@ -237,6 +244,40 @@ __device__ void stage_table(const int32_t *trow, int b0, int cnt, int NB, int32_
         const int32_t b = trow[b0 + i];
         s_tab[i] = b < 0 ? 0 : (b >= NB ? NB - 1 : b);
     }
+}
+
+// Append mode: the workgroup whose token range ends at n writes the newest
+// token's K and V rows of its kv head into the slot of position n - 1 ([Kwon]
+// §3.4 "Kernel-Level Optimizations", item 1: the new token's keys and values
+// go to the block and slot the table names).  Its own attention reads that
+// token from k_new / v_new, so nothing waits for the write.
+template <typename T, int D>
+__device__ void append_write(const DecodeArgs &a, const int32_t *trow, int s, int h, int n,
+                             int64_t head0, int tid) {
+    constexpr int VPR = D * (int)sizeof(T) / 16;  // 16-byte pieces of a row
+    if (tid >= VPR) return;
+    const int last = n - 1;
+    int32_t b = trow[last >> a.log2B];
+    b = b < 0 ? 0 : (b >= a.NB ? a.NB - 1 : b);
+    const int64_t dst = head0 + (int64_t)b * a.blk_bytes +
+                        (int64_t)(last & ((1 << a.log2B) - 1)) * a.tok_bytes + tid * 16;
+    const int64_t src = ((int64_t)s * a.Hkv + h) * D * (int64_t)sizeof(T) + tid * 16;
+    *reinterpret_cast<vec4 *>(a.k_w + dst) = load_cached(a.k_new + src);
+    *reinterpret_cast<vec4 *>(a.v_w + dst) = load_cached(a.v_new + src);
+}
+
+// The VALU kernel's form of the same write: the caller already holds its
+// 16-byte pieces of the rows (piece_off = the piece's byte offset in a row).
+__device__ __forceinline__ void append_store(const DecodeArgs &a, const int32_t *trow, int n,
+                                             int64_t head0, uint32_t piece_off, vec4 kn,
+                                             vec4 vn) {
+    const int last = n - 1;
+    int32_t b = trow[last >> a.log2B];
+    b = b < 0 ? 0 : (b >= a.NB ? a.NB - 1 : b);
+    const int64_t dst = head0 + (int64_t)b * a.blk_bytes +
+                        (int64_t)(last & ((1 << a.log2B) - 1)) * a.tok_bytes + piece_off;
+    *reinterpret_cast<vec4 *>(a.k_w + dst) = kn;
+    *reinterpret_cast<vec4 *>(a.v_w + dst) = vn;
 }
 
 // Which sequence a workgroup serves.  Without ranking, the first table chunk
@@ -337,13 +378,17 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     const char *kh = a.k + head0;
     const char *vh = a.v + head0;
 
-    const int nblk = (te - tb + B - 1) >> a.log2B;
+    // Append mode: the workgroup whose range ends at n takes position n - 1
+    // from k_new / v_new after the loop, so the loop stops before it.
+    const bool app = MODE != kDense && a.k_new != nullptr && te == n;
+    const int le = app ? te - 1 : te;
+    const int nblk = (le - tb + B - 1) >> a.log2B;
     const int chunk_blocks = MODE == kDense ? nblk : kTableChunk;
 
     for (int cb = 0; cb < nblk; cb += chunk_blocks) {
         const int cn = min(chunk_blocks, nblk - cb);
         const int ctb = tb + cb * B;                 // first token of this chunk
-        const int cte = min(te, ctb + cn * B);       // one past its last token
+        const int cte = min(le, ctb + cn * B);       // one past its last token
         if constexpr (MODE != kDense) {
             __syncthreads();  // the previous chunk's readers are done / the first chunk is out
             if (!(cb == 0 && staged)) {
@@ -460,6 +505,15 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
         }
     }
 
+    // Append mode: this lane's 16-byte pieces of the newest K and V rows,
+    // issued before the row-group merge so that it hides their latency.
+    vec4 kn = {}, vn = {};
+    const int64_t nsrc = ((int64_t)s * a.Hkv + h) * D * (int64_t)sizeof(T) + chunk_off;
+    if (app && wave == 0) {
+        kn = load_cached(a.k_new + nsrc);
+        vn = load_cached(a.v_new + nsrc);
+    }
+
     // Merge the R row groups of the wave (lanes rg*LPR + c, same c).
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
@@ -477,6 +531,26 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
             }
             m[g] = mn;
         }
+    }
+
+    if (app && wave == 0) {
+        // Every row group of wave 0 now holds the wave's merged state: add
+        // position n - 1 as one more online-softmax step, and store its rows
+        // in their slot (lanes 0 .. LPR - 1 hold the whole row).
+        float vf[EPL];
+        E::widen(vn, vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float x = group_sum<LPR>(E::dot(qv[g], kn)) * a.qk_scale;
+            const float mn = fmaxf(m[g], x);
+            const float alpha = fexp2(m[g] - mn);
+            const float pn = fexp2(x - mn);
+            l[g] = l[g] * alpha + pn;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(pn, vf[e], acc[g][e] * alpha);
+            m[g] = mn;
+        }
+        if (lane < LPR) append_store(a, trow, n, head0, chunk_off, kn, vn);
     }
 
     // Merge the waves through LDS: red[w][g][0..D) = acc, [D] = m, [D+1] = l.
@@ -698,6 +772,23 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
                 row = (int64_t)s_tab[(t - ctb) >> a.log2B] * a.blk_bytes +
                       (int64_t)(t & (B - 1)) * a.tok_bytes;
             }
+            if constexpr (MODE != kDense) {
+                // Append mode, the step that holds position n - 1 (a
+                // wave-uniform test): that position's lanes load from k_new /
+                // v_new instead, still one load per piece.
+                if (a.k_new && (unsigned)(n - 1 - t0) < (unsigned)kStepTokens) {
+                    const bool mine = t0 + r == n - 1;
+                    const int64_t src = ((int64_t)s * a.Hkv + h) * D * 2;
+                    const char *kq = mine ? a.k_new + src : kh + row;
+                    const char *vq = mine ? a.v_new + src : vh + row;
+#pragma unroll
+                    for (int i = 0; i < KL; ++i) {
+                        kb_[i] = load_cached(kq + coff[i]);
+                        vb_[i] = load_cached(vq + coff[i]);
+                    }
+                    return;
+                }
+            }
 #pragma unroll
             for (int i = 0; i < KL; ++i) {
                 kb_[i] = load_cached(kh + row + coff[i]);
@@ -781,6 +872,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     // same max and partial sums over their tokens.
     lsum += __shfl_xor(lsum, 16, 64);
     lsum += __shfl_xor(lsum, 32, 64);
+
+    if constexpr (MODE != kDense)
+        if (a.k_new && te == n) append_write<T, D>(a, trow, s, h, n, head0, tid);
 
     __syncthreads();  // table and V tiles are dead; reuse the LDS
     float *red = reinterpret_cast<float *>(smem);
@@ -990,6 +1084,10 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.ws_acc = l.PS ? l.ws : nullptr;
     a.ws_ml = l.PS ? l.ws + units * l.D : nullptr;
     a.qk_scale = l.scale * kLog2e;
+    a.k_new = (const char *)l.k_new;
+    a.v_new = (const char *)l.v_new;
+    a.k_w = (char *)l.k_w;
+    a.v_w = (char *)l.v_w;
     a.S = l.S;
     a.Hq = l.Hq;
     a.Hkv = l.Hkv;

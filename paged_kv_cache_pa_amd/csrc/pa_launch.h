@@ -23,6 +23,10 @@ struct DecodeLaunch {
     int64_t pos_stride;      // dense only: max_seq_len
     int32_t layout;          // 0 token-major, 1 head-major
     bool dense;
+    // Append mode (paged only): newest token rows [S, Hkv, D] written to
+    // position n - 1 of each sequence through k_w / v_w while attending.
+    const void *k_new = nullptr, *v_new = nullptr;
+    void *k_w = nullptr, *v_w = nullptr;
 };
 
 // Returns 0 on success, else the hipError_t of the failed launch.

@@ -129,6 +129,28 @@ def test_workspace_size_formula():
         pa.pa_decode_workspace_size(params(dtype=9))
 
 
+def test_decode_append_checks(L):
+    b = Buf()
+    p = params()
+    f = ctypes.c_float(1.0)
+    args = [b.p, b.p, b.p, b.p, b.p, b.p, b.p]
+    assert L.pa_decode_append(*args, f, b.p, ctypes.byref(params(dtype=9)), None, 0,
+                              None) == DTYPE
+    for i in (1, 2):
+        a = list(args)
+        a[i] = None
+        assert L.pa_decode_append(*a, f, b.p, ctypes.byref(p), None, 0, None) == NULL
+        a[i] = b.odd
+        assert L.pa_decode_append(*a, f, b.p, ctypes.byref(p), None, 0, None) == ALIGN
+    a = list(args)
+    a[3] = None   # k_cache
+    assert L.pa_decode_append(*a, f, b.p, ctypes.byref(p), None, 0, None) == NULL
+    assert L.pa_decode_append(*args, f, b.p, ctypes.byref(params(partition_size=32)), None, 0,
+                              None) == WS
+    assert L.pa_decode_append(None, None, None, None, None, None, None, f, None,
+                              ctypes.byref(params(num_seqs=0)), None, 0, None) == OK
+
+
 def test_zero_sequences_is_a_no_op(L):
     p = params(num_seqs=0)
     assert L.pa_decode(None, None, None, None, None, ctypes.c_float(1.0), None, ctypes.byref(p),
