@@ -787,8 +787,8 @@ def traffic_from_counters(launch_bytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--partition", type=int, default=0,
                     help="split-K partition size for pa_decode (0 = none)")
     ap.add_argument("--replicas", type=int, default=4,
@@ -869,29 +869,25 @@ def main():
     ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    def run(first, count, timed):
-        """Steps first .. first+count-1 in groups of R batches; a step is one
-        pa_decode_append launch (the new token of every sequence written to
-        its slot, then attention over the batch); batch b of a group uses
-        pool replica b, and the launches of a group are timed together with
-        one event pair."""
-        spans = []
-        i = first
-        while i < first + count:
-            g = min(R, first + count - i)
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            for b in range(g):
-                k, v = pools[b]
-                pa.pa_decode_append(q, k_new, v_new, k, v, bt, cl, p.scale, out,
-                                    max_context_len=mcl, partition_size=args.partition,
-                                    workspace=ws, layout=args.layout)
-            if timed:
-                e1.record(stream)
-                spans.append((e0, e1, g))
-            i += g
-        return spans
+    def run(count, timed):
+        """count steps back to back; step i is one pa_decode_append launch on
+        pool replica i % R (each sequence's new token written to its slot,
+        then attention over the batch).  With timed, one HIP event pair on the
+        launch stream brackets all of them: nothing but the launches runs
+        between the events, so (e1 - e0) / count is the average launch time.
+        Returns the event pair."""
+        e0 = e1 = None
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        for i in range(count):
+            k, v = pools[i % R]
+            pa.pa_decode_append(q, k_new, v_new, k, v, bt, cl, p.scale, out,
+                                max_context_len=mcl, partition_size=args.partition,
+                                workspace=ws, layout=args.layout)
+        if timed:
+            e1.record(stream)
+        return e0, e1
 
     def run_two_launch(count):
         """The same step as two launches (pa_cache_write, then pa_decode):
@@ -906,15 +902,14 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t) / count
 
-    run(0, args.warmup, False)
+    run(args.warmup, False)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
     t0 = time.perf_counter()
-    spans = run(0, args.steps, True)
+    e0, e1 = run(args.steps, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_total = sum(a.elapsed_time(b) * 1e-3 for a, b, _ in spans)
-    dec_avg = dec_total / args.steps
+    dec_avg = e0.elapsed_time(e1) * 1e-3 / args.steps
     log(f"timed {args.steps} steps: {wall / args.steps * 1e3:.4f} ms/step, "
         f"decode avg {dec_avg * 1e6:.2f} us per launch")
     # (left out of --no-extras runs, so that a kernel trace of one holds only
@@ -959,7 +954,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": launch_bytes,
             "avg_launch_us": round(dec_avg * 1e6, 3),
-            "timing": "HIP events around groups of back-to-back decode launches on the launch stream",
+            "timing": "one HIP event pair around all timed launches (back to back) on the launch stream",
         },
         "two_launch_ms_per_step": None if two_launch is None else round(two_launch * 1e3, 5),
     }
