@@ -93,9 +93,11 @@ def replicas_for(nbytes, floor=2, target=1 << 30, cap=64):
 def paged_dense_ratio(points, rounds=15, warm=3):
     """Config 3: paged vs dense decode on identical values, in both layouts
     (token-major: the pool is the dense buffer cut into blocks; head-major:
-    both transposed to [.., Hkv, tokens, D]).  Each measurement times R
-    back-to-back launches over R replicas between one event pair; paged and
-    dense alternate round by round; medians are reported."""
+    both transposed to [.., Hkv, tokens, D]).  paged_us / dense_us: R
+    launches over R replicas captured in a HIP graph, replayed between one
+    event pair (median over rounds), which measures the GPU also where a
+    launch is shorter than the host's per-call cost.  eager_*: the same R
+    launches issued from Python (host-bound for the small points)."""
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -134,11 +136,14 @@ def paged_dense_ratio(points, rounds=15, warm=3):
             for _ in range(rounds):
                 tp.append(time_group(paged, R, st))
                 td.append(time_group(dense, R, st))
-            mp, md = float(np.median(tp)), float(np.median(td))
+            ep, ed = float(np.median(tp)), float(np.median(td))
+            mp = time_graph(paged, R, rounds, st)
+            md = time_graph(dense, R, rounds, st)
             res[f"{layout} {batch}x{ctx}"] = {
                 "paged_us": round(mp * 1e6, 2), "dense_us": round(md * 1e6, 2),
                 "ratio": round(mp / md, 4), "paged_GB_s": round(nbytes / mp / 1e9, 1),
-                "replicas": R}
+                "replicas": R, "eager_paged_us": round(ep * 1e6, 2),
+                "eager_dense_us": round(ed * 1e6, 2)}
             del pk, dk
         del d, out
         torch.cuda.empty_cache()
@@ -157,6 +162,41 @@ def time_group(fn, n, stream):
     b.record(stream)
     b.synchronize()
     return a.elapsed_time(b) * 1e-3 / n
+
+
+def time_graph(fn, n, rounds, stream):
+    """Median seconds per call of fn(0) .. fn(n-1) captured once into a HIP
+    graph and replayed ``rounds`` times, each replay between one event pair
+    on ``stream``.  A short launch costs the host more (Python binding and
+    runtime, ~12 us) than the GPU; a replay launches all n kernels without
+    host work in between, so this measures the GPU."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(n):  # first calls outside the capture
+            fn(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3 / n)
+    del g
+    return float(np.median(ts))
 
 
 def copy_blocks_rate(rounds=15):
@@ -182,11 +222,13 @@ def copy_blocks_rate(rounds=15):
 
     for i in range(R):
         f(i)
-    t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+    te = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+    t = time_graph(f, R, rounds, st)
     n = p.block_pairs.shape[0]
     nbytes = 2 * 2 * n * 16 * 40 * 128 * 2 + 8 * n
     return {"pairs": int(n), "us": round(t * 1e6, 2), "GB_s": round(nbytes / t / 1e9, 1),
-            "replicas": R}
+            "replicas": R, "timing": "HIP graph of R launches, replayed",
+            "eager_us": round(te * 1e6, 2)}
 
 
 def hbm_reference(rounds=10, gib=1):

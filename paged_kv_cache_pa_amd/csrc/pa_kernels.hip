@@ -639,6 +639,11 @@ struct Mma<_Float16> {
         return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
                                                      __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
     }
+    __device__ static vec4 ones() { return vec4{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u}; }
+    __device__ static float4_t pv32(vec4 a, vec4 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a),
+                                                      __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+    }
     __device__ static vec2 pack(float x0, float x1, float x2, float x3) {
         half4_t h = {(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
         return __builtin_bit_cast(vec2, h);
@@ -656,6 +661,11 @@ struct Mma<__bf16> {
     __device__ static float4_t pv(vec2 a, vec2 b, float4_t c) {
         return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
                                                          __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+    }
+    __device__ static vec4 ones() { return vec4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u}; }
+    __device__ static float4_t pv32(vec4 a, vec4 b, float4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, a),
+                                                       __builtin_bit_cast(bf168_t, b), c, 0, 0, 0);
     }
     __device__ static vec2 pack(float x0, float x1, float x2, float x3) {
         typedef __bf16 bf164_t __attribute__((ext_vector_type(4)));
@@ -725,7 +735,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
 #pragma unroll
     for (int d = 0; d < DS; ++d) acc[d] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint32_t tok_bytes = (uint32_t)a.tok_bytes;
     uint32_t coff[KL];  // byte offset of this lane's 16 bytes inside a token row
 #pragma unroll
     for (int i = 0; i < KL; ++i) coff[i] = (uint32_t)((32 * i + 8 * kb) * 2);
@@ -1201,23 +1210,27 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
 //
 // One workgroup of 4 waves per (query head, sequence, 128-row tile of its
 // chunk); each wave owns two 16-row column tiles, which share every K and
-// V^T operand it reads from LDS.  The workgroup walks the keys in tiles of 16
-// (head dim 128) or 32 (head dim 64) tokens: each thread loads one 16-byte
-// piece of K and one of V per 16 keys, two tiles ahead of the one being
-// computed, the tile is written to one of two LDS buffers (one barrier per
-// tile), and for each 16-key sub-tile every wave computes its score tiles on
-// matrix cores as
-// S^T = K Q^T (K from LDS as the A operand, Q^T held in registers), updates
-// its running softmax per query column, and accumulates O^T += V^T P^T with
-// V^T read from LDS by the transposing ds_read_b64_tr_b16 (lane l addresses
-// row l / 4, columns d0 + 4 (l % 4), and receives V[4 (l / 16) + j][d0 + l %
-// 16], the A-operand layout) and P^T reused in place as the B operand.  The
-// causal mask and the chunk's end are applied per score.  The running max
-// of a query column moves only when a score exceeds it by more than 2^8
-// (weights then stay <= 256, exact in fp16 / bf16, and the final division
-// by the running sum is unchanged in exact arithmetic), so the accumulator
-// rescale -- 32 multiplies per lane on matrix-core results -- runs in a
-// rare wave-uniform branch instead of on every tile.  fp16 and bf16.
+// V^T operand it reads from LDS.  The workgroup walks the keys in LDS tiles
+// of 64: the tile's K and V rows go from the pool straight into LDS (16-byte
+// LDS DMA per lane, no registers), one tile ahead of the one being computed,
+// two stages, one barrier per tile.  Rows are stored unpadded with their
+// 16-byte pieces permuted per row (an XOR swizzle) so that the operand reads
+// below hit distinct banks.  For each pair of 16-key sub-tiles (32 keys) a
+// wave computes its score tiles on matrix cores as S^T = K Q^T (K from LDS as
+// the A operand, Q^T held in registers), updates its running softmax per
+// query column, and accumulates O^T += V^T P^T on 16x16x32 products whose
+// k-slots hold keys 4 kb .. 4 kb + 3 of both sub-tiles: V^T comes from LDS
+// through the transposing ds_read_b64_tr_b16 (lane l addresses row l / 4,
+// columns d0 + 4 (l % 4), and receives V[4 (l / 16) + j][d0 + l % 16], the
+// A-operand layout), and the score tiles' weights, packed, are the B operand
+// as they stand.  The weights' sum per query column is one more product, with
+// an all-ones A operand, so it is formed from the same rounded weights as the
+// output.  The causal mask and the chunk's end are applied only on the pairs
+// that need them.  The running max of a query column moves only when a score
+// exceeds it by more than 2^8 (weights then stay <= 256, exact in fp16 /
+// bf16, and the final division by the running sum is unchanged in exact
+// arithmetic), so the accumulator rescale runs in a rare wave-uniform branch
+// instead of on every tile.  fp16 and bf16.
 struct PrefillArgs {
     const char *q, *k, *v;
     const int32_t *tables, *lens, *qstart;
@@ -1230,35 +1243,59 @@ struct PrefillArgs {
 constexpr int kPrefillWaves = 4;
 constexpr float kLazy = 8.0f;    // log2 of the largest weight before a rescale
 constexpr int kPrefillCols = 2;  // 16-row column tiles per wave
-// 16-key sub-tiles per LDS tile (one barrier per tile): as few as give every
-// thread a whole 16-byte piece of K and of V to load
-constexpr int prefill_sub(int D) { return D == 64 ? 2 : 1; }
+constexpr int kPrefillKeys = 64;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillRows = 16 * kPrefillCols * kPrefillWaves;  // query rows per workgroup
 static_assert(kPrefillRows == kPrefillTileRows, "the host checks grid z with kPrefillTileRows");
 
 typedef short short4_t2 __attribute__((ext_vector_type(4)));
 
-template <typename T, int D, int NQ, int KS>
-__global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs a) {
+// 16 bytes per lane from global memory straight into LDS: lane i's piece
+// lands at LDS byte address lds + 16 i (lds wave-uniform).  M0 carries the
+// LDS address and is restored afterwards.  The load counts in vmcnt like any
+// other vector load; the compiler does not track it, so the caller waits
+// (lds_dma_wait) before any wave reads what it wrote.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+    uint32_t save;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(g), "s"(lds)
+        : "memory");
+}
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Position of 16-byte piece p of K / V row r in the LDS tile: p ^ swz(r).
+// Rows are stored unpadded; the swizzle spreads the pieces that one read
+// phase touches over distinct banks: 16 rows at one piece (the K operand)
+// and 8 rows x 2 adjacent pieces (the transposing V read).
+template <int D>
+__device__ __forceinline__ int prefill_swz(int r) {
+    if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
+template <typename T, int D, int NQ>
+__global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillArgs a) {
     using E = Elem<T>;
     using M = Mma<T>;
     constexpr int KL = D / 32;           // 32-dim slices of the score product
     constexpr int DS = D / 16;           // 16-dim slices of the output
-    // Padded LDS rows: a K row shifts 4 banks (16 lanes read 16 rows x 16 B),
-    // a V row 8 banks (32 lanes of the transposing read cover 8 rows x 32 B).
-    constexpr int KROW = D * 2 + 16, VROW = D * 2 + 32;
-    constexpr int KTILE = 16 * KROW, VTILE = 16 * VROW;
-    constexpr int CPR = D * 2 / 16;      // 16-byte pieces per row
-    constexpr int KT = 16 * KS;          // keys per LDS tile (KS sub-tiles of 16)
+    constexpr int ROWB = D * 2;          // bytes per K / V row
+    constexpr int CPR = ROWB / 16;       // 16-byte pieces per row
+    constexpr int KT = kPrefillKeys;     // keys per LDS tile: two pairs of 16-key sub-tiles
+    constexpr int TILEB = KT * ROWB;     // bytes of K (or V) per tile
+    constexpr int RPI = 64 / CPR;        // rows per DMA instruction
+    constexpr int NI = KT / RPI / kPrefillWaves;  // DMA instructions per wave per tensor
+    static_assert(NI * RPI * kPrefillWaves == KT, "whole DMA instructions per wave");
     constexpr int WROWS = 16 * NQ;       // query rows per wave
     constexpr int GROWS = WROWS * kPrefillWaves;
-    constexpr int PIECES = KS * 16 * CPR;               // per tile, of K (and of V)
-    constexpr int PPT = PIECES / (kPrefillWaves * 64);  // per thread
-    static_assert(PPT >= 1 && PPT * kPrefillWaves * 64 == PIECES, "whole pieces per thread");
 
     __shared__ int32_t s_tab[kTableChunk];
-    __shared__ __attribute__((aligned(16))) char s_k[2][KS * KTILE];  // [buffer][keys]
-    __shared__ __attribute__((aligned(16))) char s_v[2][KS * VTILE];
+    __shared__ __attribute__((aligned(16))) char s_kv[2][2][TILEB];  // [stage][K, V][tile]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1301,167 +1338,200 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
             qb[c][i] = r < rows ? load_cached(a.q + (qrow * D + 32 * i + 8 * kb) * 2)
                                 : vec4{0u, 0u, 0u, 0u};
     }
+    // The q loads complete here: a wait for them must not fall inside the key
+    // loop, where it would also wait for the LDS DMA in flight.
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+        for (int i = 0; i < KL; ++i) asm volatile("" ::"v"(qb[c][i]));
 
-    float m[NQ], lsum[NQ];
-    float4_t acc[NQ][DS];
+    float m[NQ];
+    float4_t acc[NQ][DS], accl[NQ];
+    const vec4 ones = M::ones();
+    const int mask_free_rows = n - rows + r0;  // keys up to here are visible to every row
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
         m[c] = kNegBig;
-        lsum[c] = 0.0f;
+        accl[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < DS; ++d) acc[c][d] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
+
+    // Loop-invariant LDS offsets of this lane's operand reads (within a
+    // 16-row sub-tile): K slice i (row col, piece 4 i + kb) and the
+    // transposing V^T read of slice d (row lane / 4, bytes 32 d + 8 (lane % 4)).
+    uint32_t koff[KL], voff[DS];
+#pragma unroll
+    for (int i = 0; i < KL; ++i)
+        koff[i] = col * ROWB + (((4 * i + kb) ^ prefill_swz<D>(col)) << 4);
+#pragma unroll
+    for (int d = 0; d < DS; ++d)
+        voff[d] = (lane >> 2) * ROWB + (((2 * d + ((lane & 3) >> 1)) ^ prefill_swz<D>(lane >> 2)) << 4) +
+                  8 * (lane & 1);
 
     const int B = 1 << a.log2B;
     const int32_t *trow = a.tables + (int64_t)s * a.MBS;
     const int64_t head0 = (int64_t)g * a.head_bytes;
     const int nblk = (nkeys + B - 1) >> a.log2B;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&s_kv[0][0][0];
 
-    // The KS * 16 rows of a tile are PIECES 16-byte pieces of K (and as many
-    // of V); thread tid moves pieces tid, tid + 256, ...
-    struct Regs {
-        vec4 k[PPT], v[PPT];
-    };
     for (int cb = 0; cb < nblk; cb += kTableChunk) {
         const int cn = nblk - cb < kTableChunk ? nblk - cb : kTableChunk;
         const int ck0 = cb << a.log2B;
         const int ck1 = (cb + cn) << a.log2B < nkeys ? (cb + cn) << a.log2B : nkeys;
         const int nst = (ck1 - ck0 + KT - 1) / KT;
+        const int mask_free = min(mask_free_rows, ck1 - 1);
         __syncthreads();  // the previous chunk's readers are done
         stage_table(trow, cb, cn, a.NB, s_tab, tid, blockDim.x);
         __syncthreads();
 
-        // Loads of tile j (keys clamped to the chunk, so tiles past the end
-        // reload its last key: every fetch is unconditional and each wait
-        // names exactly the set it needs).
-        auto fetch = [&](Regs &r, int j) {
+        // DMA of tile j (keys clamped to the chunk, so rows past its end
+        // reload its last key) into stage st: instruction ins of the tile
+        // fills rows ins * RPI .. + RPI - 1; lane l the piece at position
+        // l % CPR of its row, i.e. global piece (l % CPR) ^ swz(row).
+        auto issue = [&](int j, int st) {
 #pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int pc = tid + i * kPrefillWaves * 64;
-                int t = ck0 + KT * j + pc / CPR;
+            for (int i = 0; i < NI; ++i) {
+                const int ins = wave * NI + i;
+                const int r = ins * RPI + lane / CPR;
+                int t = ck0 + KT * j + r;
                 t = t < ck1 ? t : ck1 - 1;
-                const int64_t row = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
+                const int64_t off = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
                                     (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
-                                    (pc % CPR) * 16;
-                r.k[i] = load_cached(a.k + row);
-                r.v[i] = load_cached(a.v + row);
+                                    (((lane % CPR) ^ prefill_swz<D>(r)) << 4);
+                const uint32_t dk = lds0 + (uint32_t)((st * 2 + 0) * TILEB + ins * 1024);
+                const uint32_t dv = lds0 + (uint32_t)((st * 2 + 1) * TILEB + ins * 1024);
+                lds_dma16(a.k + off, __builtin_amdgcn_readfirstlane(dk));
+                lds_dma16(a.v + off, __builtin_amdgcn_readfirstlane(dv));
             }
         };
-        auto stash = [&](const Regs &r, int buf) {
+
+        // One pair of 16-key sub-tiles (keys key0 .. key0 + 31, rows 16 u ..
+        // 16 u + 31 of stage st).
+        auto pair = [&](int st, int u, int key0) {
+            const char *kt = &s_kv[st][0][0] + 16 * u * ROWB;
+            const char *vt = &s_kv[st][1][0] + 16 * u * ROWB;
+            const bool two = key0 + 16 <= w_last;  // wave-uniform
+            // A operand of O^T += V^T P^T over 32 keys: lane l holds keys
+            // 4 kb .. 4 kb + 3 of both sub-tiles (k-slots 8 kb .. 8 kb + 7)
+            vec4 va[DS];
 #pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                const int pc = tid + i * kPrefillWaves * 64;
-                const int key = pc / CPR;  // 0 .. KT - 1
-                const int sub = key >> 4, row = key & 15, off = (pc % CPR) * 16;
-                *reinterpret_cast<vec4 *>(&s_k[buf][sub * KTILE + row * KROW + off]) = r.k[i];
-                *reinterpret_cast<vec4 *>(&s_v[buf][sub * VTILE + row * VROW + off]) = r.v[i];
+            for (int d = 0; d < DS; ++d) {
+                const short4_t2 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4_t2 __attribute__((address_space(3))) *)(vt + voff[d]));
+                const short4_t2 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4_t2 __attribute__((address_space(3))) *)(vt + 16 * ROWB + voff[d]));
+                const vec2 l2 = __builtin_bit_cast(vec2, lo), h2 = __builtin_bit_cast(vec2, hi);
+                va[d] = vec4{l2.x, l2.y, h2.x, h2.y};
             }
-        };
-        auto compute = [&](int buf, int j) {
+            float x[2][NQ][4];
+            bool grow = false;
+            const bool masked = key0 + 31 > mask_free;  // wave-uniform
 #pragma unroll
-            for (int u = 0; u < KS; ++u) {
-                const int key0 = ck0 + KT * j + 16 * u;
-                if (key0 > w_last) break;  // wave-uniform: keys past this wave's rows
-                const char *kt = s_k[buf] + u * KTILE;
-                const char *vt = s_v[buf] + u * VTILE;
-                // Both operands of the sub-tile are requested from LDS before
-                // any math, so the V^T reads overlap the score product and the
-                // softmax instead of waiting behind them.
+            for (int hh = 0; hh < 2; ++hh) {
+                if (hh == 1 && !two) {
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) x[1][c][jj] = -__builtin_inff();
+                    break;
+                }
                 vec4 ka[KL];
 #pragma unroll
                 for (int i = 0; i < KL; ++i)
-                    ka[i] = *reinterpret_cast<const vec4 *>(kt + col * KROW + (32 * i + 8 * kb) * 2);
-                vec2 va[DS];
-#pragma unroll
-                for (int d = 0; d < DS; ++d) {
-                    // A operand of O^T += V^T P^T through the transposing read
-                    const char *src = vt + (lane >> 2) * VROW + (16 * d + 4 * (lane & 3)) * 2;
-                    const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (short4_t2 __attribute__((address_space(3))) *)(src));
-                    va[d] = __builtin_bit_cast(vec2, t4);
-                }
-                // Scores of this sub-tile; the running max m is moved only when a
-                // score exceeds it by more than 2^kLazy (weights then stay <=
-                // 2^kLazy, exact in fp16 and bf16), so the accumulators are
-                // rescaled rarely, in a wave-uniform branch.
-                float x[NQ][4];
-                bool grow = false;
+                    ka[i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
                     float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int i = 0; i < KL; ++i) sc = M::qk(ka[i], qb[c][i], sc);
-                    // keys key0 + 4 kb + jj with jj > lim are hidden (causal, or
-                    // past the chunk's end)
-                    const int lim = min(my_pos[c], ck1 - 1) - (key0 + 4 * kb);
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        x[c][jj] = jj > lim ? -__builtin_inff() : sc[jj] * a.qk_scale;
-                    float mx = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
+                    for (int jj = 0; jj < 4; ++jj) x[hh][c][jj] = sc[jj] * a.qk_scale;
+                    if (masked) {
+                        // keys key0 + 16 hh + 4 kb + jj with jj > lim are hidden
+                        // (causal, or past the chunk's end)
+                        const int lim = min(my_pos[c], ck1 - 1) - (key0 + 16 * hh + 4 * kb);
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj)
+                            x[hh][c][jj] = jj > lim ? -__builtin_inff() : x[hh][c][jj];
+                    }
+                    const float mx = fmaxf(fmaxf(x[hh][c][0], x[hh][c][1]),
+                                           fmaxf(x[hh][c][2], x[hh][c][3]));
                     grow |= mx > m[c] + kLazy;
                 }
-                if (__any(grow)) {
-#pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        float mx = fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]));
-                        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                        const float mn = fmaxf(m[c], mx);
-                        const float alpha = fexp2(m[c] - mn);
-                        m[c] = mn;
-                        lsum[c] *= alpha;
-#pragma unroll
-                        for (int d = 0; d < DS; ++d) acc[c][d] = acc[c][d] * alpha;
-                    }
-                }
-                vec2 pb[NQ], pr[NQ];
+            }
+            if (__any(grow)) {
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
-                    float p[4];
+                    float mx = fmaxf(fmaxf(fmaxf(x[0][c][0], x[0][c][1]), fmaxf(x[0][c][2], x[0][c][3])),
+                                     fmaxf(fmaxf(x[1][c][0], x[1][c][1]), fmaxf(x[1][c][2], x[1][c][3])));
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    const float mn = fmaxf(m[c], mx);
+                    const float alpha = fexp2(m[c] - mn);
+                    m[c] = mn;
+                    accl[c] = accl[c] * alpha;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[c][jj] - m[c]);
-                    lsum[c] += (p[0] + p[1]) + (p[2] + p[3]);
-                    pb[c] = M::pack(p[0], p[1], p[2], p[3]);
-                    pr[c] = M::rest(p[0], p[1], p[2], p[3], pb[c]);
+                    for (int d = 0; d < DS; ++d) acc[c][d] = acc[c][d] * alpha;
                 }
+            }
+            vec4 pb[NQ], pr[NQ];
 #pragma unroll
-                for (int d = 0; d < DS; ++d) {
+            for (int c = 0; c < NQ; ++c) {
+                float p[2][4];
 #pragma unroll
-                    for (int c = 0; c < NQ; ++c) {
-                        acc[c][d] = M::pv(va[d], pb[c], acc[c][d]);
-                        if constexpr (M::kSplit) acc[c][d] = M::pv(va[d], pr[c], acc[c][d]);
-                    }
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) p[hh][jj] = fexp2(x[hh][c][jj] - m[c]);
+                const vec2 b0 = M::pack(p[0][0], p[0][1], p[0][2], p[0][3]);
+                const vec2 b1 = M::pack(p[1][0], p[1][1], p[1][2], p[1][3]);
+                pb[c] = vec4{b0.x, b0.y, b1.x, b1.y};
+                if constexpr (M::kSplit) {
+                    const vec2 e0 = M::rest(p[0][0], p[0][1], p[0][2], p[0][3], b0);
+                    const vec2 e1 = M::rest(p[1][0], p[1][1], p[1][2], p[1][3], b1);
+                    pr[c] = vec4{e0.x, e0.y, e1.x, e1.y};
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                // the weights' sum over the 32 keys, as one more output row
+                accl[c] = M::pv32(ones, pb[c], accl[c]);
+                if constexpr (M::kSplit) accl[c] = M::pv32(ones, pr[c], accl[c]);
+            }
+#pragma unroll
+            for (int d = 0; d < DS; ++d) {
+#pragma unroll
+                for (int c = 0; c < NQ; ++c) {
+                    acc[c][d] = M::pv32(va[d], pb[c], acc[c][d]);
+                    if constexpr (M::kSplit) acc[c][d] = M::pv32(va[d], pr[c], acc[c][d]);
                 }
             }
         };
-        // Two register sets: tile j + 1 is in flight while tile j is
-        // computed, and tile j + 2 is requested before it; a tile is written
-        // to LDS one compute period after its loads were issued.
-        Regs r0, r1;
-        fetch(r0, 0);
-        fetch(r1, 1);
-        stash(r0, 0);
-        __syncthreads();
-        for (int j = 0; j < nst; j += 2) {
-            fetch(r0, j + 2);
-            compute(0, j);
-            stash(r1, 1);
-            __syncthreads();  // tile j + 1 is in place; tile j's readers are done
-            if (j + 1 >= nst) break;
-            fetch(r1, j + 3);
-            compute(1, j + 1);
-            stash(r0, 0);
+
+        // Tile j: wait for this thread's DMA of it, barrier (every wave's
+        // DMA of tile j has landed, and every wave is done with tile j - 1),
+        // start tile j + 1 into the other stage, compute tile j.
+        auto step = [&](int st, int j) {
+            lds_dma_wait();
             __syncthreads();
+            if (j + 1 < nst) issue(j + 1, st ^ 1);
+            const int key0 = ck0 + KT * j;
+            if (key0 > w_last) return;  // wave-uniform: the whole tile is past this wave's rows
+            pair(st, 0, key0);
+            if (key0 + 32 <= w_last) pair(st, 2, key0 + 32);
+        };
+        issue(0, 0);
+        for (int j = 0; j < nst; j += 2) {
+            step(0, j);
+            if (j + 1 >= nst) break;
+            step(1, j + 1);
         }
     }
 
-    // The four lanes of a query column (col, col + 16, col + 32, col + 48)
-    // hold the same running max and partial sums over their keys.
+    // Every lane of a query column holds the column's full weight sum.
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        float l = lsum[c];
-        l += __shfl_xor(l, 16, 64);
-        l += __shfl_xor(l, 32, 64);
+        const float l = accl[c][0];
         const int r = r0 + 16 * c + col;
         if (r < rows) {
             const float inv = 1.0f / l;
@@ -1473,6 +1543,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void prefill_kernel(PrefillArgs
                     E::store(a.out, o + 16 * d + 4 * kb + jj, acc[c][d][jj] * inv);
         }
     }
+    // The DMA of a tile this wave did not compute (its rows end earlier) may
+    // still be in flight: let it land before the workgroup's LDS is released.
+    lds_dma_wait();
 }
 
 template <typename T>
@@ -1510,10 +1583,10 @@ static hipError_t launch_prefill_t(const PrefillLaunch &l, hipStream_t st) {
     const dim3 grid((unsigned)l.Hq, (unsigned)l.S, (unsigned)a.tiles);
     (void)hipGetLastError();  // an error left by other code is not this launch's
     if (l.D == 64)
-        hipLaunchKernelGGL((prefill_kernel<T, 64, kPrefillCols, prefill_sub(64)>), grid, dim3(kPrefillWaves * 64), 0,
+        hipLaunchKernelGGL((prefill_kernel<T, 64, kPrefillCols>), grid, dim3(kPrefillWaves * 64), 0,
                            st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<T, 128, kPrefillCols, prefill_sub(128)>), grid, dim3(kPrefillWaves * 64),
+        hipLaunchKernelGGL((prefill_kernel<T, 128, kPrefillCols>), grid, dim3(kPrefillWaves * 64),
                            0, st, a);
     return hipGetLastError();
 }
