@@ -464,6 +464,54 @@ def prefill_rate(rounds=10, d=128):
     return res
 
 
+def config_rates(rounds=10):
+    """pa_decode on the other workloads, head-major pools over replicas,
+    timed as HIP-graph replays (the GPU's time, also for short launches):
+    the tiny fp32 batch, the parallel-sampling beams (96 sequences sharing
+    prompt blocks; bytes counted per sequence as the kernel reads them) and
+    the grouped-query long-context batch with 512-token split-K (decode and
+    merge launches together)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+    import workloads as W
+
+    st = torch.cuda.current_stream()
+    res = {}
+    for label, make, ps in (("tiny fp32 (4 seqs, 8/8 heads, D 64)", lambda: W.config1(poison=False), 0),
+                            ("beams fp16 (96 seqs, 40/40 heads)", lambda: W.config4(poison=False).paged, 0),
+                            ("GQA bf16 (8 seqs to 16384, 12/2 heads, split 512)", W.config5, 512)):
+        p = make()
+        S, Hq, D = p.q.shape
+        k0, v0 = _dev_pool(p.k_cache, "HND"), _dev_pool(p.v_cache, "HND")
+        R = replicas_for(2 * k0.numel() * k0.element_size())
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+        q, bt, cl = _dev(p.q), _dev(p.block_tables), _dev(p.context_lens)
+        out = torch.empty_like(q)
+        mcl = int(p.context_lens.max())
+        params = pa.DecodeParams(S, Hq, p.num_kv_heads, D, p.block_size, p.max_blocks_per_seq,
+                                 p.num_blocks, mcl, ps, {"f32": 0, "f16": 1, "bf16": 2}[p.dtype],
+                                 pa.LAYOUTS["HND"])
+        ws = torch.empty(max(1, pa.pa_decode_workspace_size(params) // 4), dtype=torch.float32,
+                         device="cuda")
+
+        def f(i):
+            k, v = pools[i % R]
+            pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl, partition_size=ps,
+                         workspace=ws, layout="HND")
+
+        for i in range(2 * R):
+            f(i)
+        t = time_graph(f, R, rounds, st)
+        b = decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, W.ELEM_BYTES[p.dtype], p.block_size)
+        res[label] = {"us": round(t * 1e6, 2), "algorithmic_bytes": b,
+                      "GB_s": round(b / t / 1e9, 1), "frac_of_8000": round(b / t / 8e12, 4),
+                      "kv_tokens_per_s": round(float(p.context_lens.sum()) / t, 1), "replicas": R}
+        del pools, k0, v0
+        torch.cuda.empty_cache()
+    return res
+
+
 BLOCK_SWEEP_SIZES = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 
 
@@ -1001,6 +1049,11 @@ def main():
         "two_launch_ms_per_step": None if two_launch is None else round(two_launch * 1e3, 5),
     }
     if not args.no_extras:
+        try:
+            result["other_workloads"] = config_rates()
+        except Exception as e:  # report, do not lose the main line
+            result["other_workloads"] = {"error": repr(e)}
+        log("other workloads done")
         try:
             result["paged_vs_dense"] = paged_dense_ratio([(8, 256), (32, 1024), (128, 2048)])
         except Exception as e:  # report, do not hide the main result
