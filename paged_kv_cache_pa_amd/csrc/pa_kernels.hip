@@ -607,18 +607,30 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
 //   S^T = K Q^T   v_mfma_f32_16x16x32: A = K (row = token, 8 dims per lane),
 //                 B = Q^T (column = head, heads >= G are zero);
 //   O^T += V^T P^T  v_mfma_f32_16x16x16: B = P^T is the S^T result in place
-//                 (lane l holds tokens 4*(l/16)..+3 of head l%16), A = V^T is
-//                 read transposed from a per-wave LDS tile of the step's V.
+//                 (lane l holds tokens 4*(l/16)..+3 of head l%16), A = V^T
+//                 from the transposing LDS read ds_read_b64_tr_b16.
+// K and V are loaded as whole rows per instruction (the decode kernel's
+// pattern: every 128-byte line a load instruction touches is used whole by
+// it) and pass through a per-wave LDS tile of unpadded, swizzled rows, from
+// which both operands are read.  Loading the A operand of K straight from
+// the pool instead (16 rows x 64 bytes per instruction, each line split over
+// two instructions) streamed ~12% slower.
 // Lane layouts (A[l%16][k-block l/16], B[k-block l/16][l%16],
 // C[4*(l/16)+j][l%16]) were checked against a host product on gfx950.
 // The per-head running max is shared by the 16 tokens of a step (two lane
-// exchanges), so P can feed one product.  The weights enter the product in
-// the input type: fp16 once (11-bit significand), bf16 as a high part plus
-// the bf16 rounding of the remainder, two products that together carry ~16
-// significant bits (one bf16 rounding alone, 2^-9 per weight, can exceed the
-// output tolerance for short sequences).  The running sum uses the fp32
-// weights.
+// exchanges), so P can feed one product; it moves lazily (kLazy below).  The
+// weights enter the product in the input type: fp16 once (11-bit
+// significand), bf16 as a high part plus the bf16 rounding of the remainder,
+// two products that together carry ~16 significant bits (one bf16 rounding
+// alone, 2^-9 per weight, can exceed the output tolerance for short
+// sequences).  The running sum uses the fp32 weights.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t2 __attribute__((ext_vector_type(4)));
+// Lazy running max of the matrix-core kernels: the max of a score column
+// moves only when a score exceeds it by more than 2^kLazy, so weights stay
+// <= 2^kLazy (exact in fp16 / bf16), the final division by the running sum
+// is unchanged in exact arithmetic, and the accumulator rescale is rare.
+constexpr float kLazy = 8.0f;
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -680,19 +692,33 @@ struct Mma<__bf16> {
     }
 };
 
+// Position of 16-byte piece p of a K / V row r in an LDS tile of unpadded
+// rows: p ^ row_swz(r).  The swizzle spreads the pieces that one read phase
+// of the matrix-core kernels touches over distinct banks: 16 rows at one
+// piece (a K operand read) and 8 rows x 2 adjacent pieces (the transposing
+// V read).  Head dim 128 (16 pieces per row) or 64 (8).
+template <int D>
+__device__ __forceinline__ int row_swz(int r) {
+    if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
+    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+}
+
 template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a) {
     using E = Elem<T>;
     using M = Mma<T>;
     static_assert(sizeof(T) == 2 && G >= 2 && G <= 16 && D % 32 == 0, "16-bit grouped-query tile");
-    constexpr int KL = D / 32;            // 16-byte loads per step for K (and for V)
+    constexpr int KL = D / 32;            // 32-dim slices of the score product
     constexpr int DS = D / 16;            // 16-wide slices of the output rows
-    constexpr int VROW = D * 2 + 16;      // padded LDS row of a V tile (bytes)
-    constexpr int VTILE = 16 * VROW;      // one step's V tile
+    constexpr int ROWB = D * 2;           // bytes of a K / V row
+    constexpr int LPR = ROWB / 16;        // lanes per row in a load (16-byte pieces)
+    constexpr int RPL = 64 / LPR;         // rows per load instruction
+    constexpr int U = kStepTokens / RPL;  // loads per step, of K and of V
+    constexpr int TILE = kStepTokens * ROWB;  // one step's K (or V) tile
     constexpr int TAB_BYTES = kTableChunk * 4;
 
-    // Dynamic LDS (sized by the launcher): block-table chunk + one V tile per
-    // wave during the loop, then the cross-wave merge buffer.
+    // Dynamic LDS (sized by the launcher): block-table chunk + one K and one
+    // V tile per wave during the loop, then the cross-wave merge buffer.
     extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
     char *smem = dyn_smem;
     __shared__ int32_t s_len[kRankMaxSeqs];
@@ -708,7 +734,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     const int kb = lane >> 4;    // k-block: 8 dims of each 32-dim slice; 4 tokens of the score tile
     const int h = blockIdx.x % a.Hkv;
     const int part = blockIdx.y;
-    char *vtile = smem + TAB_BYTES + wave * VTILE;
+    char *ktile = smem + TAB_BYTES + wave * 2 * TILE;
+    char *vtile = ktile + TILE;
 
     int s, n;
     bool staged;
@@ -735,9 +762,21 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
 #pragma unroll
     for (int d = 0; d < DS; ++d) acc[d] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t coff[KL];  // byte offset of this lane's 16 bytes inside a token row
+    // Loads: lane l moves piece l % LPR of rows l / LPR + RPL u (whole rows
+    // per instruction, every fetched line used by it); the rows land in the
+    // wave's tiles with their pieces swizzled.
+    const int lrow = lane / LPR, lpiece = lane % LPR;
+    uint32_t soff[U];  // LDS offset of this lane's piece of load u
 #pragma unroll
-    for (int i = 0; i < KL; ++i) coff[i] = (uint32_t)((32 * i + 8 * kb) * 2);
+    for (int u = 0; u < U; ++u) {
+        const int r = lrow + RPL * u;
+        soff[u] = (uint32_t)(r * ROWB + ((lpiece ^ row_swz<D>(r)) << 4));
+    }
+    // K operand: row tok, piece 4 i + kb; transposing V read: row lane / 4,
+    // piece 2 d + (lane % 4) / 2, half lane % 2
+    const int kswz = row_swz<D>(tok), vswz = row_swz<D>(lane >> 2);
+    const uint32_t kbase = (uint32_t)(tok * ROWB), vbase = (uint32_t)((lane >> 2) * ROWB + 8 * (lane & 1));
+    const int vpc = (lane & 3) >> 1;
     const int B = 1 << a.log2B;
     const int32_t *trow = MODE == kDense ? nullptr : a.tables + (int64_t)s * a.MBS;
     const int64_t head0 = (int64_t)h * a.head_bytes + (MODE == kDense ? (int64_t)s * a.seq_bytes : 0);
@@ -761,95 +800,100 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
         const int nfull = (cte - ctb) / kStepTokens;
         const int tail = (cte - ctb) % kStepTokens;
 
-        // K and V of step j: lane loads token tok (clamped when MASKED).  Each
-        // load instruction covers 64 bytes of 16 rows (half of a 128-byte
-        // line each, the other half in the next instruction), so ordinary
-        // cached loads are used here: with the non-temporal hint this
-        // pattern ran ~10% slower.
-        auto issue = [&]<bool MASKED>(vec4 (&kb_)[KL], vec4 (&vb_)[KL], int j) {
+        // K and V of step j: load u of lane l is piece lpiece of row lrow +
+        // RPL u (rows clamped to the range when MASKED, so they re-read its
+        // last token).
+        auto issue = [&]<bool MASKED>(vec4 (&kb_)[U], vec4 (&vb_)[U], int j) {
             const int t0 = ctb + j * kStepTokens;
-            int r = tok;
-            if (MASKED) r = min(r, cte - 1 - t0);
-            int64_t row;
+            int64_t base;   // first row of the step (paged wide / dense)
             if constexpr (MODE == kDense) {
-                row = (int64_t)(t0 + r) * a.tok_bytes;
+                base = (int64_t)t0 * a.tok_bytes;
             } else if constexpr (MODE == kPagedWide) {
                 const int phys = __builtin_amdgcn_readfirstlane(s_tab[(t0 - ctb) >> a.log2B]);
-                row = (int64_t)phys * a.blk_bytes + (int64_t)((t0 & (B - 1)) + r) * a.tok_bytes;
+                base = (int64_t)phys * a.blk_bytes + (int64_t)(t0 & (B - 1)) * a.tok_bytes;
             } else {
-                const int t = t0 + r;
-                row = (int64_t)s_tab[(t - ctb) >> a.log2B] * a.blk_bytes +
-                      (int64_t)(t & (B - 1)) * a.tok_bytes;
+                base = 0;
             }
-            if constexpr (MODE != kDense) {
-                // Append mode, the step that holds position n - 1 (a
-                // wave-uniform test): that position's lanes load from k_new /
-                // v_new instead, still one load per piece.
-                if (a.k_new && (unsigned)(n - 1 - t0) < (unsigned)kStepTokens) {
-                    const bool mine = t0 + r == n - 1;
-                    const int64_t src = ((int64_t)s * a.Hkv + h) * D * 2;
-                    const char *kq = mine ? a.k_new + src : kh + row;
-                    const char *vq = mine ? a.v_new + src : vh + row;
+            // Append mode, the step that holds position n - 1 (a wave-uniform
+            // test): that row's lanes load from k_new / v_new instead.
+            const bool app = MODE != kDense && a.k_new && (unsigned)(n - 1 - t0) < (unsigned)kStepTokens;
+            const int64_t nsrc = ((int64_t)s * a.Hkv + h) * D * 2 + lpiece * 16;
 #pragma unroll
-                    for (int i = 0; i < KL; ++i) {
-                        kb_[i] = load_cached(kq + coff[i]);
-                        vb_[i] = load_cached(vq + coff[i]);
-                    }
-                    return;
+            for (int u = 0; u < U; ++u) {
+                int r = lrow + RPL * u;
+                if (MASKED) r = min(r, cte - 1 - t0);
+                int64_t row;
+                if constexpr (MODE == kPagedNarrow) {
+                    const int t = t0 + r;
+                    row = (int64_t)s_tab[(t - ctb) >> a.log2B] * a.blk_bytes +
+                          (int64_t)(t & (B - 1)) * a.tok_bytes;
+                } else {
+                    row = base + (int64_t)r * a.tok_bytes;
                 }
-            }
-#pragma unroll
-            for (int i = 0; i < KL; ++i) {
-                kb_[i] = load_cached(kh + row + coff[i]);
-                vb_[i] = load_cached(vh + row + coff[i]);
+                const char *kq = kh + row + lpiece * 16;
+                const char *vq = vh + row + lpiece * 16;
+                if (app && t0 + r == n - 1) {
+                    kq = a.k_new + nsrc;
+                    vq = a.v_new + nsrc;
+                }
+                kb_[u] = load_stream(kq);
+                vb_[u] = load_stream(vq);
             }
         };
-        auto compute = [&]<bool MASKED>(const vec4 (&kb_)[KL], const vec4 (&vb_)[KL], int j) {
-            // the step's V rows into this wave's tile; LDS operations of a wave
-            // run in order, so the previous step's reads have completed
-            char *vt = vtile;
+        auto compute = [&]<bool MASKED>(const vec4 (&kb_)[U], const vec4 (&vb_)[U], int j) {
+            // the step's K and V rows into this wave's tiles; LDS operations
+            // of a wave run in order, so the previous step's reads are done
+            // and the reads below see these writes
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                *reinterpret_cast<vec4 *>(ktile + soff[u]) = kb_[u];
+                *reinterpret_cast<vec4 *>(vtile + soff[u]) = vb_[u];
+            }
+            vec4 ka[KL];
 #pragma unroll
             for (int i = 0; i < KL; ++i)
-                *reinterpret_cast<vec4 *>(vt + tok * VROW + coff[i]) = vb_[i];
+                ka[i] = *reinterpret_cast<const vec4 *>(ktile + kbase + (((4 * i + kb) ^ kswz) << 4));
             // S^T[token 4 kb + jj][head tok]
             float4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < KL; ++i) sc = M::qk(kb_[i], qb[i], sc);
+            for (int i = 0; i < KL; ++i) sc = M::qk(ka[i], qb[i], sc);
             float x[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 x[jj] = sc[jj] * a.qk_scale;
                 if (MASKED && ctb + j * kStepTokens + 4 * kb + jj >= cte) x[jj] = -__builtin_inff();
             }
+            // lazy running max: the rescale is a rare wave-uniform branch
             float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m, mx);
-            const float alpha = fexp2(m - mn);
+            if (__any(mx > m + kLazy)) {
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float mn = fmaxf(m, mx);
+                const float alpha = fexp2(m - mn);
+                lsum *= alpha;
+#pragma unroll
+                for (int d = 0; d < DS; ++d) acc[d] = acc[d] * alpha;
+                m = mn;
+            }
             float p[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[jj] - mn);
-            lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            m = mn;
+            for (int jj = 0; jj < 4; ++jj) p[jj] = fexp2(x[jj] - m);
+            lsum += (p[0] + p[1]) + (p[2] + p[3]);
             const vec2 pb = M::pack(p[0], p[1], p[2], p[3]);
             const vec2 pr = M::rest(p[0], p[1], p[2], p[3], pb);
-            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int d = 0; d < DS; ++d) {
-                // A operand of O^T += V^T P^T: V[token 4 kb + jj][dim 16 d + tok]
-                const char *src = vt + (4 * kb) * VROW + (16 * d + tok) * 2;
-                const uint32_t v0 = *reinterpret_cast<const uint16_t *>(src);
-                const uint32_t v1 = *reinterpret_cast<const uint16_t *>(src + VROW);
-                const uint32_t v2 = *reinterpret_cast<const uint16_t *>(src + 2 * VROW);
-                const uint32_t v3 = *reinterpret_cast<const uint16_t *>(src + 3 * VROW);
-                const vec2 va = {v0 | (v1 << 16), v2 | (v3 << 16)};
-                acc[d] = acc[d] * alpha;
+                // O^T += V^T P^T: A operand V[token 4 kb + jj][dim 16 d + tok]
+                const short4_t2 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (short4_t2 __attribute__((address_space(3))) *)(vtile + vbase +
+                                                                     (((2 * d + vpc) ^ vswz) << 4)));
+                const vec2 va = __builtin_bit_cast(vec2, t4);
                 acc[d] = M::pv(va, pb, acc[d]);
                 if constexpr (M::kSplit) acc[d] = M::pv(va, pr, acc[d]);
             }
         };
 
-        vec4 ka[KL], va[KL], kc[KL], vc[KL];
+        vec4 ka[U], va[U], kc[U], vc[U];
         int j = wave;
         if (j < nfull) {
             issue.template operator()<false>(ka, va, j);
@@ -1137,7 +1181,7 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     size_t lds;
     if constexpr (sizeof(T) == 2 && G >= 2) {  // grouped-query heads: matrix cores
         auto lds_of = [&](int w) {
-            return max2((size_t)kTableChunk * 4 + (size_t)w * 16 * (2 * D + 16), red_bytes(w));
+            return max2((size_t)kTableChunk * 4 + (size_t)w * 2 * kStepTokens * 2 * D, red_bytes(w));
         };
         fn = l.dense ? decode_mma_kernel<T, D, G, kDense>
            : l.B >= kStepTokens ? decode_mma_kernel<T, D, G, kPagedWide>
@@ -1241,13 +1285,10 @@ struct PrefillArgs {
 };
 
 constexpr int kPrefillWaves = 4;
-constexpr float kLazy = 8.0f;    // log2 of the largest weight before a rescale
 constexpr int kPrefillCols = 2;  // 16-row column tiles per wave
 constexpr int kPrefillKeys = 64;  // keys per LDS tile (one barrier per tile)
 constexpr int kPrefillRows = 16 * kPrefillCols * kPrefillWaves;  // query rows per workgroup
 static_assert(kPrefillRows == kPrefillTileRows, "the host checks grid z with kPrefillTileRows");
-
-typedef short short4_t2 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from global memory straight into LDS: lane i's piece
 // lands at LDS byte address lds + 16 i (lds wave-uniform).  M0 carries the
@@ -1268,15 +1309,6 @@ __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Position of 16-byte piece p of K / V row r in the LDS tile: p ^ swz(r).
-// Rows are stored unpadded; the swizzle spreads the pieces that one read
-// phase touches over distinct banks: 16 rows at one piece (the K operand)
-// and 8 rows x 2 adjacent pieces (the transposing V read).
-template <int D>
-__device__ __forceinline__ int prefill_swz(int r) {
-    if constexpr (D == 128) return 2 * (r & 7) + ((r >> 3) & 1);
-    else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
-}
 
 template <typename T, int D, int NQ>
 __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillArgs a) {
@@ -1363,10 +1395,10 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
     uint32_t koff[KL], voff[DS];
 #pragma unroll
     for (int i = 0; i < KL; ++i)
-        koff[i] = col * ROWB + (((4 * i + kb) ^ prefill_swz<D>(col)) << 4);
+        koff[i] = col * ROWB + (((4 * i + kb) ^ row_swz<D>(col)) << 4);
 #pragma unroll
     for (int d = 0; d < DS; ++d)
-        voff[d] = (lane >> 2) * ROWB + (((2 * d + ((lane & 3) >> 1)) ^ prefill_swz<D>(lane >> 2)) << 4) +
+        voff[d] = (lane >> 2) * ROWB + (((2 * d + ((lane & 3) >> 1)) ^ row_swz<D>(lane >> 2)) << 4) +
                   8 * (lane & 1);
 
     const int B = 1 << a.log2B;
@@ -1398,7 +1430,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                 t = t < ck1 ? t : ck1 - 1;
                 const int64_t off = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
                                     (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
-                                    (((lane % CPR) ^ prefill_swz<D>(r)) << 4);
+                                    (((lane % CPR) ^ row_swz<D>(r)) << 4);
                 const uint32_t dk = lds0 + (uint32_t)((st * 2 + 0) * TILEB + ins * 1024);
                 const uint32_t dv = lds0 + (uint32_t)((st * 2 + 1) * TILEB + ins * 1024);
                 lds_dma16(a.k + off, __builtin_amdgcn_readfirstlane(dk));
