@@ -289,6 +289,42 @@ def copy_layers_rate(rounds=10, layers=40):
             "GB_s": round(nbytes / t / 1e9, 1), "launches": -(-layers // 64)}
 
 
+def write_layers_rate(rounds=10, layers=40, tokens=64):
+    """pa_cache_write_layers: one decode iteration's new rows (64 sequences)
+    for all 40 layers of OPT-13B in one launch, against 40 pa_cache_write
+    launches; both timed as HIP-graph replays (GPU time).  Pools of 256
+    blocks per layer (head-major), distinct random slots."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    nb, B, H, D = 256, 16, 40, 128
+    g = torch.Generator(device="cuda").manual_seed(808)
+    ks = [torch.empty((nb, H, B, D), dtype=torch.float16, device="cuda") for _ in range(layers)]
+    vs = [torch.empty_like(k) for k in ks]
+    kn = [torch.randn((tokens, H, D), generator=g, device="cuda").half() for _ in range(layers)]
+    vn = [torch.randn((tokens, H, D), generator=g, device="cuda").half() for _ in range(layers)]
+    slots = torch.from_numpy(np.random.default_rng(9).permutation(nb * B)[:tokens]
+                             .astype(np.int32)).cuda()
+    st = torch.cuda.current_stream()
+
+    def one(i):
+        pa.pa_cache_write_layers(kn, vn, ks, vs, slots, layout="HND")
+
+    def per_layer(i):
+        for layer in range(layers):
+            pa.pa_cache_write(kn[layer], vn[layer], ks[layer], vs[layer], slots, layout="HND")
+
+    t1 = time_graph(one, 1, rounds, st)
+    tn = time_graph(per_layer, 1, rounds, st)
+    nbytes = 2 * 2 * tokens * H * D * 2 * layers + 4 * tokens
+    del ks, vs, kn, vn
+    torch.cuda.empty_cache()
+    return {"tokens": tokens, "layers": layers, "one_launch_us": round(t1 * 1e6, 1),
+            "one_launch_GB_s": round(nbytes / t1 / 1e9, 1),
+            "per_layer_launches_us": round(tn * 1e6, 1)}
+
+
 def swap_rate(rounds=5, mib=64):
     """Swapping between HBM and pinned host memory at block sizes 16 / 64 /
     256 tokens (OPT-13B layer geometry, 40 heads x 128 dims fp16): one
@@ -1065,7 +1101,8 @@ def main():
             result["copy_blocks"] = {"error": repr(e)}
         log("copy_blocks done")
         for key, fn in (("hbm_reference", hbm_reference),
-                        ("copy_blocks_layers", copy_layers_rate), ("swap", swap_rate),
+                        ("copy_blocks_layers", copy_layers_rate),
+                        ("cache_write_layers", write_layers_rate), ("swap", swap_rate),
                         ("block_manager", block_manager_rate), ("prefill", prefill_rate)):
             try:
                 result[key] = fn()

@@ -240,6 +240,24 @@ int pa_copy_blocks_layers(void *const *k_caches, void *const *v_caches, int32_t 
                           const pa_cache_params *p, void *stream);
 
 /*
+ * cache_write for every layer of a model at once: layer l's new rows
+ * k_new[l], v_new[l] ([num_tokens, Hkv, D] each) go to the slots of
+ * slot_mapping in layer l's pools k_caches[l], v_caches[l].  One slot
+ * mapping serves all layers, because a block id names the same position in
+ * every layer's pool ([Res] "A paged KV cache, in code"); the writes of all
+ * layers run in one launch per 64 layers (the fused write of [Kwon] §3.4
+ * "Kernel-Level Optimizations", item 1, across layers, as item 3 fuses the
+ * copies).  Same rules per layer as pa_cache_write.
+ * k_new, v_new, k_caches, v_caches: HOST arrays of num_layers device
+ * pointers, read during the call only; all pools have the geometry ``p``.
+ * slot_mapping: device pointer.  num_tokens == 0 enqueues nothing.
+ */
+int pa_cache_write_layers(const void *const *k_new, const void *const *v_new,
+                          void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                          const int32_t *slot_mapping, int32_t num_tokens,
+                          const pa_cache_params *p, void *stream);
+
+/*
  * swap_blocks: moves whole blocks between two pools of the same block
  * geometry, for every layer, in one launch per 64 layers: for each pair
  * (src, dst), layer l: dst_k[l][dst] = src_k[l][src], dst_v[l][dst] =

@@ -207,6 +207,16 @@ def copy_blocks_layers(k_caches, v_caches, block_pairs, dtype, layout="NHD"):
     return [k for k, _ in out], [v for _, v in out]
 
 
+def cache_write_layers(k_news, v_news, k_caches, v_caches, slot_mapping, dtype, layout="NHD"):
+    """cache_write applied to every layer: layer l's rows into layer l's
+    pools at the one slot mapping ([Res] "A paged KV cache, in code": a
+    block id names the same position in every layer's pool).  Returns new
+    lists of pools."""
+    out = [cache_write(kn, vn, k, v, slot_mapping, dtype, layout)
+           for kn, vn, k, v in zip(k_news, v_news, k_caches, v_caches)]
+    return [k for k, _ in out], [v for _, v in out]
+
+
 def swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs):
     """Whole blocks from one pool into another, every layer ([Kwon] §3.4
     "Scheduling and Preemption": swapping copies a group's blocks to the CPU

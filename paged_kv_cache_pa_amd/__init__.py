@@ -20,7 +20,8 @@ import os
 from .build import LIB_PATH
 
 __all__ = ["pa_decode", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
-           "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill", "PaError",
+           "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers", "pa_swap_blocks",
+           "pa_prefill", "PaError",
            "lib",
            "LIB_PATH", "STATUS"]
 
@@ -100,12 +101,14 @@ def lib():
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
         L.pa_copy_blocks.argtypes = [P, P, P, I32, CP, P]
         L.pa_copy_blocks_layers.argtypes = [P, P, I32, P, I32, CP, P]
+        L.pa_cache_write_layers.argtypes = [P, P, P, P, I32, P, I32, CP, P]
         L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                  ctypes.POINTER(PrefillParams), P]
         L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
         for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_append", "pa_decode_dense",
                   "pa_cache_write",
-                  "pa_copy_blocks", "pa_copy_blocks_layers", "pa_swap_blocks", "pa_prefill"):
+                  "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers",
+                  "pa_swap_blocks", "pa_prefill"):
             getattr(L, f).restype = ctypes.c_int
         L.pa_status_string.argtypes = [ctypes.c_int]
         L.pa_status_string.restype = ctypes.c_char_p
@@ -349,6 +352,27 @@ def pa_copy_blocks_layers(k_caches, v_caches, block_pairs, *, stream=None, layou
                                        len(k_caches), _ptr(block_pairs),
                                        int(block_pairs.shape[0]), ctypes.byref(p),
                                        _stream(stream)), "pa_copy_blocks_layers")
+
+
+def pa_cache_write_layers(k_news, v_news, k_caches, v_caches, slot_mapping, *, stream=None,
+                          layout="NHD"):
+    """pa_cache_write for every layer (lists of [N, Hkv, D] rows and of
+    [NB, ...] pools, one slot mapping) in one launch per 64 layers."""
+    import torch
+
+    _pools(k_caches, v_caches, "pa_cache_write_layers")
+    if len(k_news) != len(k_caches) or len(v_news) != len(k_caches):
+        raise ValueError("pa_cache_write_layers: one K and one V row tensor per layer")
+    _need(slot_mapping, "slot_mapping", 1, torch.int32)
+    p = _cache_params(k_caches[0], layout)
+    for t in list(k_news) + list(v_news):
+        _need(t, "k_new / v_new", 3, k_caches[0].dtype)
+        if tuple(t.shape) != (slot_mapping.shape[0], p.num_kv_heads, p.head_dim):
+            raise ValueError("pa_cache_write_layers: rows must be [N, Hkv, D], N = len(slot_mapping)")
+    _check(lib().pa_cache_write_layers(_ptr_array(k_news), _ptr_array(v_news),
+                                       _ptr_array(k_caches), _ptr_array(v_caches), len(k_caches),
+                                       _ptr(slot_mapping), int(slot_mapping.shape[0]),
+                                       ctypes.byref(p), _stream(stream)), "pa_cache_write_layers")
 
 
 def pa_swap_blocks(dst_k, dst_v, src_k, src_v, block_pairs, *, stream=None, layout="NHD"):

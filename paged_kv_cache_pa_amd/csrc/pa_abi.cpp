@@ -302,6 +302,40 @@ int pa_copy_blocks(void *k_cache, void *v_cache, const int32_t *block_pairs, int
     return pa_copy_blocks_layers(k, v, 1, block_pairs, num_pairs, p, stream);
 }
 
+int pa_cache_write_layers(const void *const *k_new, const void *const *v_new,
+                          void *const *k_caches, void *const *v_caches, int32_t num_layers,
+                          const int32_t *slot_mapping, int32_t num_tokens,
+                          const pa_cache_params *p, void *stream) {
+    const int st = check_cache_params(p);
+    if (st != PA_OK) return st;
+    if (num_tokens < 0 || num_layers < 1) return PA_ERR_SHAPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_caches || !v_caches || !slot_mapping) return PA_ERR_NULL;
+    for (int32_t l = 0; l < num_layers; ++l) {
+        if (!k_new[l] || !v_new[l] || !k_caches[l] || !v_caches[l]) return PA_ERR_NULL;
+        if (!aligned16(k_new[l]) || !aligned16(v_new[l]) || !aligned16(k_caches[l]) ||
+            !aligned16(v_caches[l]))
+            return PA_ERR_ALIGN;
+    }
+    if ((uintptr_t)slot_mapping & 3u) return PA_ERR_ALIGN;
+    const int64_t row = (int64_t)p->head_dim * elem_bytes(p->dtype);  // one head's row
+    pa::CacheWriteLayers w;
+    for (int32_t l0 = 0; l0 < num_layers; l0 += pa::kMaxLayers) {
+        w.layers = num_layers - l0 < pa::kMaxLayers ? num_layers - l0 : pa::kMaxLayers;
+        for (int32_t l = 0; l < w.layers; ++l) {
+            w.k_new[l] = k_new[l0 + l];
+            w.v_new[l] = v_new[l0 + l];
+            w.k_cache[l] = k_caches[l0 + l];
+            w.v_cache[l] = v_caches[l0 + l];
+        }
+        const int e = pa::launch_cache_write_layers(w, slot_mapping, num_tokens, p->num_blocks,
+                                                    p->block_size, p->num_kv_heads, row,
+                                                    p->layout, stream);
+        if (e) return hip_status(e);
+    }
+    return PA_OK;
+}
+
 int pa_copy_blocks_layers(void *const *k_caches, void *const *v_caches, int32_t num_layers,
                           const int32_t *block_pairs, int32_t num_pairs,
                           const pa_cache_params *p, void *stream) {

@@ -1637,11 +1637,14 @@ int launch_prefill(const PrefillLaunch &l, void *stream) {
 // layout given by the strides.  Out-of-range slots are skipped ([Kwon] §3.4
 // "Kernel-Level Optimizations", item 1: one fused launch writes every new
 // token to the block and slot the scheduler names).
-__global__ __launch_bounds__(kThreads) void cache_write_kernel(
-    const vec4 *__restrict__ k_new, const vec4 *__restrict__ v_new, char *__restrict__ k_cache,
-    char *__restrict__ v_cache, const int32_t *__restrict__ slots, int64_t total, int64_t rv,
-    int32_t hkv, int32_t log2B, int64_t num_slots, int64_t blk_bytes, int64_t tok_bytes,
-    int64_t head_bytes) {
+// The new tokens' K and V rows into their slots: work item idx moves one
+// 16-byte piece (token i, K or V, kv head g, piece x), grid-strided.
+__device__ __forceinline__ void write_rows(const vec4 *__restrict__ k_new,
+                                           const vec4 *__restrict__ v_new, char *__restrict__ k_cache,
+                                           char *__restrict__ v_cache,
+                                           const int32_t *__restrict__ slots, int64_t total, int64_t rv,
+                                           int32_t hkv, int32_t log2B, int64_t num_slots,
+                                           int64_t blk_bytes, int64_t tok_bytes, int64_t head_bytes) {
     const int64_t per_tensor = (int64_t)hkv * rv;    // vectors of K (or V) per token
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total; idx += stride) {
@@ -1660,24 +1663,68 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     }
 }
 
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(
+    const vec4 *__restrict__ k_new, const vec4 *__restrict__ v_new, char *__restrict__ k_cache,
+    char *__restrict__ v_cache, const int32_t *__restrict__ slots, int64_t total, int64_t rv,
+    int32_t hkv, int32_t log2B, int64_t num_slots, int64_t blk_bytes, int64_t tok_bytes,
+    int64_t head_bytes) {
+    write_rows(k_new, v_new, k_cache, v_cache, slots, total, rv, hkv, log2B, num_slots, blk_bytes,
+               tok_bytes, head_bytes);
+}
+
+// Every layer's new rows in one launch: grid y = layer.
+__global__ __launch_bounds__(kThreads) void cache_write_layers_kernel(
+    CacheWriteLayers w, const int32_t *__restrict__ slots, int64_t total, int64_t rv, int32_t hkv,
+    int32_t log2B, int64_t num_slots, int64_t blk_bytes, int64_t tok_bytes, int64_t head_bytes) {
+    const int l = blockIdx.y;
+    write_rows((const vec4 *)w.k_new[l], (const vec4 *)w.v_new[l], (char *)w.k_cache[l],
+               (char *)w.v_cache[l], slots, total, rv, hkv, log2B, num_slots, blk_bytes, tok_bytes,
+               head_bytes);
+}
+
+// Launch geometry and pool strides shared by the single- and multi-layer
+// writes.
+struct WriteGeom {
+    int64_t rv, total, blk_bytes, tok_bytes, head_bytes, blocks;
+    int log2B;
+};
+static WriteGeom write_geom(int32_t n, int32_t block_size, int32_t hkv, int64_t row_bytes,
+                            int32_t layout) {
+    WriteGeom g;
+    g.rv = row_bytes / 16;  // vectors per head row
+    g.total = (int64_t)n * 2 * hkv * g.rv;
+    g.log2B = 0;
+    while ((1 << g.log2B) < block_size) ++g.log2B;
+    g.blk_bytes = row_bytes * hkv * block_size;
+    g.tok_bytes = layout == 0 ? row_bytes * hkv : row_bytes;
+    g.head_bytes = layout == 0 ? row_bytes : row_bytes * block_size;
+    g.blocks = (g.total + kThreads * 4 - 1) / (kThreads * 4);
+    if (g.blocks > 65536) g.blocks = 65536;
+    if (g.blocks < 1) g.blocks = 1;
+    return g;
+}
+
 int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
                        const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
                        int32_t hkv, int64_t row_bytes, int32_t layout, void *stream) {
-    const int64_t rv = row_bytes / 16;  // vectors per head row
-    const int64_t total = (int64_t)n * 2 * hkv * rv;
-    int log2B = 0;
-    while ((1 << log2B) < block_size) ++log2B;
-    const int64_t blk_bytes = row_bytes * hkv * block_size;
-    const int64_t tok_bytes = layout == 0 ? row_bytes * hkv : row_bytes;
-    const int64_t head_bytes = layout == 0 ? row_bytes : row_bytes * block_size;
-    int64_t blocks = (total + kThreads * 4 - 1) / (kThreads * 4);
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
+    const WriteGeom g = write_geom(n, block_size, hkv, row_bytes, layout);
     (void)hipGetLastError();  // an error left by other code is not this launch's
-    hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)g.blocks), dim3(kThreads), 0,
                        (hipStream_t)stream, (const vec4 *)k_new, (const vec4 *)v_new,
-                       (char *)k_cache, (char *)v_cache, slots, total, rv, hkv, log2B,
-                       (int64_t)num_blocks * block_size, blk_bytes, tok_bytes, head_bytes);
+                       (char *)k_cache, (char *)v_cache, slots, g.total, g.rv, hkv, g.log2B,
+                       (int64_t)num_blocks * block_size, g.blk_bytes, g.tok_bytes, g.head_bytes);
+    return (int)hipGetLastError();
+}
+
+int launch_cache_write_layers(const CacheWriteLayers &w, const int32_t *slots, int32_t n,
+                              int32_t num_blocks, int32_t block_size, int32_t hkv,
+                              int64_t row_bytes, int32_t layout, void *stream) {
+    const WriteGeom g = write_geom(n, block_size, hkv, row_bytes, layout);
+    (void)hipGetLastError();  // an error left by other code is not this launch's
+    hipLaunchKernelGGL(cache_write_layers_kernel, dim3((unsigned)g.blocks, (unsigned)w.layers),
+                       dim3(kThreads), 0, (hipStream_t)stream, w, slots, g.total, g.rv, hkv,
+                       g.log2B, (int64_t)num_blocks * block_size, g.blk_bytes, g.tok_bytes,
+                       g.head_bytes);
     return (int)hipGetLastError();
 }
 

@@ -56,9 +56,23 @@ int launch_cache_write(const void *k_new, const void *v_new, void *k_cache, void
                        const int32_t *slots, int32_t n, int32_t num_blocks, int32_t block_size,
                        int32_t hkv, int64_t row_bytes, int32_t layout, void *stream);
 
-// Whole-block moves between two pools (or within one) for up to
-// kMaxLayers layers; passed by value as the kernel argument.
+// Most layers one launch of a multi-layer entry point takes (the pointer
+// arrays travel by value in the kernel argument).
 constexpr int kMaxLayers = 64;
+
+// New rows of every layer (up to kMaxLayers per launch): per layer the
+// token rows [n, Hkv, D] and the pools; one slot mapping for all layers.
+struct CacheWriteLayers {
+    const void *k_new[kMaxLayers], *v_new[kMaxLayers];
+    void *k_cache[kMaxLayers], *v_cache[kMaxLayers];
+    int32_t layers;  // 1 .. kMaxLayers
+};
+int launch_cache_write_layers(const CacheWriteLayers &w, const int32_t *slots, int32_t n,
+                              int32_t num_blocks, int32_t block_size, int32_t hkv,
+                              int64_t row_bytes, int32_t layout, void *stream);
+
+// Whole-block moves between two pools (or within one) for up to
+// kMaxLayers layers.
 struct BlockMove {
     const void *src_k[kMaxLayers], *src_v[kMaxLayers];
     void *dst_k[kMaxLayers], *dst_v[kMaxLayers];

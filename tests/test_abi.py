@@ -237,6 +237,16 @@ def test_multi_layer_copy_and_swap_checks(L):
                                    None) == DTYPE
     # too many (pair, layer, K|V) workgroups for one grid dimension
     assert L.pa_copy_blocks_layers(good, good, 3, b.p, 1 << 30, ctypes.byref(p), None) == UNSUP
+    cw = L.pa_cache_write_layers
+    assert cw(good, good, good, good, 3, b.p, 0, ctypes.byref(p), None) == OK
+    assert cw(good, good, good, good, 0, b.p, 2, ctypes.byref(p), None) == SHAPE
+    assert cw(good, good, good, good, 3, b.p, -1, ctypes.byref(p), None) == SHAPE
+    assert cw(good, None, good, good, 3, b.p, 2, ctypes.byref(p), None) == NULL
+    assert cw(good, good, arr(b.p, b.p, None), good, 3, b.p, 2, ctypes.byref(p), None) == NULL
+    assert cw(arr(b.p, b.odd, b.p), good, good, good, 3, b.p, 2, ctypes.byref(p), None) == ALIGN
+    assert cw(good, good, good, good, 3, None, 2, ctypes.byref(p), None) == NULL
+    assert cw(good, good, good, good, 3, P(b.p.value + 2), 2, ctypes.byref(p), None) == ALIGN
+    assert cw(good, good, good, good, 3, b.p, 2, ctypes.byref(cparams(dtype=9)), None) == DTYPE
     sw = L.pa_swap_blocks
     assert sw(good, good, 8, good, good, 64, 3, b.p, 0, ctypes.byref(p), None) == OK
     assert sw(good, good, 0, good, good, 64, 3, b.p, 2, ctypes.byref(p), None) == SHAPE

@@ -127,6 +127,36 @@ def test_copy_blocks_layers_bit_exact(layers):
         assert same_bits(to_host(vd[layer], dt), vc[layer])
 
 
+@pytest.mark.parametrize("layers,dtype,layout,B", [(3, "f16", "HND", 16), (70, "bf16", "NHD", 4),
+                                                   (5, "f32", "HND", 1)])
+def test_cache_write_layers_bit_exact(layers, dtype, layout, B):
+    """Every layer's new rows in one call (70 layers: two launches), against
+    the oracle layer by layer; padding slots (-1) and slots past the pool are
+    skipped (the oracle gets only the valid ones)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    rng = np.random.default_rng(54)
+    NB, H, D, N = 40, 2, 64, 23   # NB * B >= N at every block size
+    ks = [in_layout(W.nan_fill((NB, B, H, D), dtype), layout) for _ in range(layers)]
+    vs = [in_layout(W.nan_fill((NB, B, H, D), dtype), layout) for _ in range(layers)]
+    kn = [W.randn(rng, (N, H, D), dtype) for _ in range(layers)]
+    vn = [W.randn(rng, (N, H, D), dtype) for _ in range(layers)]
+    slots = rng.permutation(NB * B)[:N].astype(np.int32)
+    slots[3], slots[9], slots[17] = -1, NB * B, NB * B + 7
+    kd, vd = [to_dev(x, dtype) for x in ks], [to_dev(x, dtype) for x in vs]
+    pa.pa_cache_write_layers([to_dev(x, dtype) for x in kn], [to_dev(x, dtype) for x in vn],
+                             kd, vd, to_dev(slots), layout=layout)
+    torch.cuda.synchronize()
+    keep = (slots >= 0) & (slots < NB * B)
+    kc, vc = oracle.cache_write_layers([x[keep] for x in kn], [x[keep] for x in vn], ks, vs,
+                                       slots[keep], dtype, layout=layout)
+    for layer in range(layers):
+        assert same_bits(to_host(kd[layer], dtype), kc[layer]), layer
+        assert same_bits(to_host(vd[layer], dtype), vc[layer]), layer
+
+
 @pytest.mark.parametrize("dtype,layout", [("bf16", "HND"), ("f32", "NHD")])
 def test_swap_out_and_in_through_pinned_host_pools(dtype, layout):
     import torch

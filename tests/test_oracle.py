@@ -508,6 +508,28 @@ def test_copy_blocks_layers_is_per_layer_copy():
         assert same_bits(kc[layer], ke) and same_bits(vc[layer], ve)
 
 
+def test_cache_write_layers_fig6(golden):
+    """Fig. 6's slots in three layers at once: layer l's token i lands at the
+    printed slot of layer l's pools only (values 100 l + i), every other
+    slot of every layer stays NaN."""
+    g = golden("fig6_block_table.json")
+    B, NB, n = g["block_size"], g["num_blocks"], g["context_len"]
+    slots = np.array(g["slots"], np.int32)
+    D, L = 8, 3
+    pools = [empty_pool(NB, B, 1, D, "f32") for _ in range(L)]
+    news = [np.full((n, 1, D), 100.0 * layer, np.float32) + np.arange(n, dtype=np.float32)[:, None, None]
+            for layer in range(L)]
+    kc, vc = oracle.cache_write_layers(news, [-x for x in news], [k for k, _ in pools],
+                                       [v for _, v in pools], slots, "f32")
+    for layer in range(L):
+        written = np.zeros((NB, B), bool)
+        for i, sl in enumerate(g["slots"]):
+            assert (kc[layer][sl // B, sl % B] == 100.0 * layer + i).all()
+            assert (vc[layer][sl // B, sl % B] == -(100.0 * layer + i)).all()
+            written[sl // B, sl % B] = True
+        assert np.isnan(kc[layer][~written]).all() and np.isnan(vc[layer][~written]).all()
+
+
 def test_index_errors_write_nothing():
     k, v = empty_pool(4, 4, 1, 8, "f32")
     new = np.ones((2, 1, 8), np.float32)
