@@ -86,7 +86,8 @@ typedef enum {
 typedef struct {
     int32_t num_seqs;           /* S >= 0; S == 0 enqueues nothing           */
     int32_t num_q_heads;        /* Hq >= 1                                    */
-    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 8     */
+    int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0; Hq / Hkv <= 8,    */
+                                /* <= 16 for fp16 / bf16 (PA_ERR_UNSUPPORTED) */
     int32_t head_dim;           /* D in {64, 128}                             */
     int32_t block_size;         /* B, a power of two in [1, 256]; paged only  */
     int32_t max_blocks_per_seq; /* row stride of block_tables; paged only     */

@@ -47,7 +47,10 @@ int check_decode_shape(const pa_decode_params *p, int64_t row_limit, int32_t gra
     if (p->partition_size < 0 || (p->partition_size && p->partition_size % granule))
         return PA_ERR_SHAPE;
     if (p->head_dim != 64 && p->head_dim != 128) return PA_ERR_UNSUPPORTED;
-    if (p->num_q_heads / p->num_kv_heads > 8) return PA_ERR_UNSUPPORTED;
+    // Up to 8 query heads per kv head in every type; up to 16 in fp16 / bf16
+    // (the matrix-core kernel's score tile has 16 head columns).
+    const int32_t group = p->num_q_heads / p->num_kv_heads;
+    if (group > 16 || (group > 8 && p->dtype == PA_F32)) return PA_ERR_UNSUPPORTED;
     // In-step row offsets are 32-bit: 16 token rows must span under 4 GiB.
     if ((int64_t)p->num_kv_heads * p->head_dim * elem_bytes(p->dtype) > (1 << 27))
         return PA_ERR_UNSUPPORTED;

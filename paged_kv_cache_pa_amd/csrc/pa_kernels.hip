@@ -1223,6 +1223,20 @@ static hipError_t launch_g(const DecodeLaunch &l, hipStream_t st) {
         case 7: return launch_typed<T, D, 7>(l, st);
         case 8: return launch_typed<T, D, 8>(l, st);
     }
+    // 9 .. 16 query heads per kv head: 16-bit types only, on the matrix
+    // cores, whose score tile has 16 head columns
+    if constexpr (sizeof(T) == 2) {
+        switch (l.Hq / l.Hkv) {
+            case 9: return launch_typed<T, D, 9>(l, st);
+            case 10: return launch_typed<T, D, 10>(l, st);
+            case 11: return launch_typed<T, D, 11>(l, st);
+            case 12: return launch_typed<T, D, 12>(l, st);
+            case 13: return launch_typed<T, D, 13>(l, st);
+            case 14: return launch_typed<T, D, 14>(l, st);
+            case 15: return launch_typed<T, D, 15>(l, st);
+            case 16: return launch_typed<T, D, 16>(l, st);
+        }
+    }
     return hipErrorInvalidValue;
 }
 
@@ -1782,7 +1796,7 @@ const char *hip_error_name(int err) { return hipGetErrorName((hipError_t)err); }
 
 const char *kernel_build_info() {
     return "gfx950; decode: 256 threads (4 wave64), 16-token wave steps, non-temporal K/V loads, "
-           "LDS block table, longest-first order up to 256 sequences, G in 1..8, D in {64,128}, "
+           "LDS block table, longest-first order up to 256 sequences, G in 1..8 (1..16 for 16-bit types), D in {64,128}, "
            "fp32/fp16/bf16, token- or head-major blocks; cache_write / copy_blocks: 16-byte vectors";
 }
 

@@ -86,7 +86,9 @@ def decode(L, p, q=None, k=None, v=None, t=None, c=None, out=None, ws=None, nbyt
     (dict(layout=2), SHAPE), (dict(layout=-1), SHAPE),
     (dict(head_dim=96), UNSUP), (dict(head_dim=256), UNSUP),
     (dict(num_kv_heads=1 << 20, num_q_heads=1 << 20), UNSUP),
-    (dict(num_q_heads=18, num_kv_heads=2), UNSUP),
+    (dict(num_q_heads=18, num_kv_heads=2), UNSUP),            # fp32: at most 8 per kv head
+    (dict(num_q_heads=34, num_kv_heads=2, dtype=1), UNSUP),   # fp16: at most 16
+    (dict(num_q_heads=34, num_kv_heads=2, dtype=2), UNSUP),   # bf16: at most 16
 ])
 def test_decode_rejects_bad_shapes(L, kw, code):
     assert decode(L, params(**kw)) == code

@@ -1,6 +1,6 @@
 """Seeded random sweep over the whole parameter space, against the fp64
 oracle: data type, head dim, query / kv heads (every group size the
-matrix-core kernel takes and the VALU one), block size, pool layout,
+matrix-core kernel takes, up to 16, and the VALU one), block size, pool layout,
 split-K partition size, lengths (including 0, 1 and block edges), for
 pa_decode, pa_decode_append and pa_prefill.  Each case is small enough for
 the oracle; the case's parameters are printed before it runs."""
@@ -31,7 +31,7 @@ def draw(seed):
     r = np.random.default_rng(1000 + seed)
     dtype = ["f32", "f16", "bf16"][seed % 3]
     D = int(r.choice([64, 128]))
-    G = int(r.integers(1, 9))
+    G = int(r.integers(1, 9 if dtype == "f32" else 17))   # up to 16 on the matrix cores
     hkv = int(r.integers(1, 4))
     B = int(2 ** r.integers(0, 9))
     S = int(r.integers(1, 7))

@@ -227,11 +227,22 @@ def test_block_sizes(B, layout):
         check(p, got, ref_decode(p), f"block size {B} {layout} ps {ps}")
 
 
-@pytest.mark.parametrize("G", range(1, 9))
+@pytest.mark.parametrize("G", range(1, 17))
 def test_head_groups(G):
     p = W.random_paged(23, "bf16", [5, 77, 300], 2 * G, 2, 64)
     check(p, run_decode(p), ref_decode(p), f"G={G}")
     check(p, run_decode(p, partition_size=64), ref_decode(p), f"G={G} split")
+
+
+@pytest.mark.parametrize("G", [12, 16])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_wide_head_groups_f16_d128(G, layout):
+    """9..16 query heads per kv head (16-bit types, matrix cores), head dim
+    128, with split-K and a ragged batch."""
+    p = W.random_paged(29, "f16", [1, 16, 17, 513, 1000], 4 * G, 4, 128)
+    for ps in (0, 256):
+        check(p, run_decode(p, partition_size=ps, layout=layout), ref_decode(p),
+              f"G={G} {layout} ps {ps}")
 
 
 @pytest.mark.parametrize("dtype", W.DTYPES)
