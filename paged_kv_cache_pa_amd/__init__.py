@@ -140,6 +140,9 @@ def _stream(stream):
     if stream is None:
         import torch
 
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:  # the current stream's handle without a Stream object (~0.1 us)
+            return ctypes.c_void_p(raw(torch._C._cuda_getDevice()))
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
@@ -186,7 +189,8 @@ def pa_decode_workspace_size(params: DecodeParams) -> int:
 def _workspace(params, workspace, device):
     import torch
 
-    need = pa_decode_workspace_size(params)
+    # no split: no workspace (the size query is skipped, it would return 0)
+    need = pa_decode_workspace_size(params) if params.partition_size else 0
     if need and workspace is None:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=device)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
