@@ -994,12 +994,29 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     const int qh = blockIdx.x;  // s * Hq + h
     const int s = qh / Hq;
     const int t = threadIdx.x;
-    const int n = clamp_len(lens[s], max_ctx);
-    const int np = (n + PS - 1) / PS;
-    if (np <= 1) return;
     const float *ml = ws_ml + (int64_t)qh * P * 2;
     const float4 *ac = reinterpret_cast<const float4 *>(ws_acc + (int64_t)qh * P * D);
     const int c = t % C4, pg = t / C4;
+    // Up to NG * kMergeRegs partitions the partials are requested together
+    // with the length (addresses clamped to the P allocated partitions, so
+    // they do not wait for it); entries past the sequence's own partitions
+    // are dropped by selects below.
+    const bool regs = P <= NG * kMergeRegs;
+    float mp[kMergeRegs], lp[kMergeRegs];
+    float4 x[kMergeRegs];
+    if (regs) {
+#pragma unroll
+        for (int k = 0; k < kMergeRegs; ++k) {
+            int pc = pg + k * NG;
+            pc = pc < P ? pc : P - 1;
+            mp[k] = ml[2 * pc];
+            lp[k] = ml[2 * pc + 1];
+            x[k] = ac[(int64_t)pc * C4 + c];
+        }
+    }
+    const int n = clamp_len(lens[s], max_ctx);
+    const int np = (n + PS - 1) / PS;
+    if (np <= 1) return;
 
     auto block_max = [&](float x) {
 #pragma unroll
@@ -1014,19 +1031,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
 
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float lsum = 0.0f;
-    if (np <= NG * kMergeRegs) {
-        float mp[kMergeRegs], lp[kMergeRegs];
-        float4 x[kMergeRegs];
+    if (regs) {
 #pragma unroll
         for (int k = 0; k < kMergeRegs; ++k) {
-            const int p = pg + k * NG;
-            const bool ok = p < np;
-            const int pc = ok ? p : np - 1;  // every load stays inside this row's partials
-            const float m0 = ml[2 * pc], l0 = ml[2 * pc + 1];
-            const float4 x0 = ac[(int64_t)pc * C4 + c];
-            mp[k] = ok ? m0 : kNegBig;
-            lp[k] = ok ? l0 : 0.0f;
-            x[k] = ok ? x0 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const bool ok = pg + k * NG < np;
+            mp[k] = ok ? mp[k] : kNegBig;
+            lp[k] = ok ? lp[k] : 0.0f;
+            x[k] = ok ? x[k] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         float mx = kNegBig;
 #pragma unroll
