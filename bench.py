@@ -38,16 +38,16 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_opt13b_f16_counters.json"
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_pa_amd", "csrc", "pa_kernels.hip")
 
 
-# How the committed profile summaries are made (run from the repository root).
+# How the committed profile summaries are made (run from the repository root;
+# OUT is any scratch directory for the raw rocprofv3 output).
 PROFILE_COMMANDS = [
-    "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_trace -o trace -- "
+    "rocprofv3 --kernel-trace --stats -f csv -d OUT/prof_trace -o trace -- "
     "python3 bench.py --steps 30 --warmup 5 --no-extras",
-    "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/prof_fetch -o fetch -- "
-    "python3 bench.py --counters-run --steps 5 > gpurun_out/prof_fetch.log",
-    "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/prof_write -o write -- "
-    "python3 bench.py --counters-run --steps 5 > gpurun_out/prof_write.log",
-    "python3 bench.py --summarize-profiles gpurun_out/prof_trace gpurun_out/prof_fetch "
-    "gpurun_out/prof_write profiles",
+    "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/prof_fetch -o fetch -- "
+    "python3 bench.py --counters-run --steps 5 > OUT/prof_fetch.log",
+    "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/prof_write -o write -- "
+    "python3 bench.py --counters-run --steps 5 > OUT/prof_write.log",
+    "python3 bench.py --summarize-profiles OUT/prof_trace OUT/prof_fetch OUT/prof_write profiles",
 ]
 
 
@@ -873,7 +873,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, commands):
         json.dump(counters, f, indent=1)
     lines = ["# Kernel trace: OPT-13B-shape decode step (fp16, head-major pool; "
              "pa_decode_append: newest token stored, then attention, one launch)", "",
-             "Command (from the repository root, on one MI355X):", "", "```",
+             "Command (from the repository root, on one MI355X; OUT is a scratch directory for the raw output):", "", "```",
              commands[0], "```", "",
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in stats:
