@@ -1446,20 +1446,27 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
         // reload its last key) into stage st: instruction ins of the tile
         // fills rows ins * RPI .. + RPI - 1; lane l the piece at position
         // l % CPR of its row, i.e. global piece (l % CPR) ^ swz(row).
+        // The table entries are all read before the first DMA: the DMA's asm
+        // orders memory, so a read placed after one would wait for it.
         auto issue = [&](int j, int st) {
+            int64_t off[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int ins = wave * NI + i;
                 const int r = ins * RPI + lane / CPR;
                 int t = ck0 + KT * j + r;
                 t = t < ck1 ? t : ck1 - 1;
-                const int64_t off = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
-                                    (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
-                                    (((lane % CPR) ^ row_swz<D>(r)) << 4);
+                off[i] = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
+                         (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
+                         (((lane % CPR) ^ row_swz<D>(r)) << 4);
+            }
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int ins = wave * NI + i;
                 const uint32_t dk = lds0 + (uint32_t)((st * 2 + 0) * TILEB + ins * 1024);
                 const uint32_t dv = lds0 + (uint32_t)((st * 2 + 1) * TILEB + ins * 1024);
-                lds_dma16(a.k + off, __builtin_amdgcn_readfirstlane(dk));
-                lds_dma16(a.v + off, __builtin_amdgcn_readfirstlane(dv));
+                lds_dma16(a.k + off[i], __builtin_amdgcn_readfirstlane(dk));
+                lds_dma16(a.v + off[i], __builtin_amdgcn_readfirstlane(dv));
             }
         };
 
@@ -1484,6 +1491,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
             float x[2][NQ][4];
             bool grow = false;
             const bool masked = key0 + 31 > mask_free;  // wave-uniform
+            // K operands of both sub-tiles, requested together (the second
+            // sub-tile's rows are in LDS whether or not they are used)
+            vec4 ka2[2][KL];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < KL; ++i)
+                    ka2[hh][i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 if (hh == 1 && !two) {
@@ -1493,10 +1508,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                         for (int jj = 0; jj < 4; ++jj) x[1][c][jj] = -__builtin_inff();
                     break;
                 }
-                vec4 ka[KL];
-#pragma unroll
-                for (int i = 0; i < KL; ++i)
-                    ka[i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
+                const vec4 *ka = ka2[hh];
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
                     float4_t sc = {0.f, 0.f, 0.f, 0.f};
