@@ -1127,12 +1127,14 @@ static int64_t resident_workgroups(const void *fn, int nw, size_t lds) {
 // but only while every workgroup is still resident at once: a grid that
 // spills into a second round of workgroups finishes in two round trips of
 // the longest workgroup.  So: 8 waves when the whole grid fits at 8; else 4
-// when it fits at 4; else (a grid several times the machine) 4.
+// when it fits at 4; else 8 for a grid under 1024 workgroups (fewer rounds
+// of shorter workgroups) if 8-wave workgroups fit at all, and 4 beyond.
 static int pick_waves(const void *fn8, const void *fn4, int64_t wgs, size_t lds8, size_t lds4) {
     if (fn8 == nullptr) return 4;
-    if (wgs <= resident_workgroups(fn8, 8, lds8)) return 8;
+    const int64_t r8 = resident_workgroups(fn8, 8, lds8);  // 0 if 8 waves cannot be resident
+    if (wgs <= r8) return 8;
     if (wgs <= resident_workgroups(fn4, 4, lds4)) return 4;
-    return wgs < 1024 ? 8 : 4;
+    return wgs < 1024 && r8 > 0 ? 8 : 4;
 }
 
 template <typename T, int D, int G>
