@@ -1041,6 +1041,21 @@ def main():
     # (left out of --no-extras runs, so that a kernel trace of one holds only
     # the fused launches)
     two_launch = None if args.no_extras else run_two_launch(max(args.steps, 10))
+    # Spread: the timed region repeated after the measurement (not part of
+    # value), one event pair per repeat.
+    spread = None
+    if not args.no_extras:
+        per = []
+        for _ in range(10):
+            a0, a1 = run(args.steps, True)
+            torch.cuda.synchronize()
+            per.append(a0.elapsed_time(a1) * 1e3 / args.steps)
+        spread = {"repeats": len(per), "steps_each": args.steps,
+                  "launch_us_median": round(float(np.median(per)), 3),
+                  "launch_us_p10": round(float(np.percentile(per, 10)), 3),
+                  "launch_us_p90": round(float(np.percentile(per, 90)), 3),
+                  "what": "the timed region repeated after the measurement; average launch "
+                          "time of each repeat (HIP events on the launch stream)"}
 
     toks = int(lens.sum())
     value = toks * args.steps / wall
@@ -1083,6 +1098,7 @@ def main():
             "timing": "one HIP event pair around all timed launches (back to back) on the launch stream",
         },
         "two_launch_ms_per_step": None if two_launch is None else round(two_launch * 1e3, 5),
+        "launch_spread": spread,
     }
     if not args.no_extras:
         try:
