@@ -500,13 +500,14 @@ def prefill_rate(rounds=10, d=128):
     return res
 
 
-def config_rates(rounds=10):
+def config_rates(rounds=10, only=None):
     """pa_decode on the other workloads, head-major pools over replicas,
     timed as HIP-graph replays (the GPU's time, also for short launches):
     the tiny fp32 batch, the parallel-sampling beams (96 sequences sharing
     prompt blocks; bytes counted per sequence as the kernel reads them) and
     the grouped-query long-context batch with 512-token split-K (decode and
-    merge launches together)."""
+    merge launches together).  ``only``: time just the workloads whose label
+    starts with it."""
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -517,6 +518,8 @@ def config_rates(rounds=10):
     for label, make, ps in (("tiny fp32 (4 seqs, 8/8 heads, D 64)", lambda: W.config1(poison=False), 0),
                             ("beams fp16 (96 seqs, 40/40 heads)", lambda: W.config4(poison=False).paged, 0),
                             ("GQA bf16 (8 seqs to 16384, 12/2 heads, split 512)", W.config5, 512)):
+        if only is not None and not label.startswith(only):
+            continue
         p = make()
         S, Hq, D = p.q.shape
         k0, v0 = _dev_pool(p.k_cache, "HND"), _dev_pool(p.v_cache, "HND")
@@ -927,6 +930,9 @@ def main():
                     help="short run for rocprofv3 --pmc passes (decode launches + calibration copy)")
     ap.add_argument("--prefill", action="store_true",
                     help="time pa_prefill (chunked prompt attention) only; one JSON line")
+    ap.add_argument("--gqa", action="store_true",
+                    help="time pa_decode on the grouped-query long-context batch only (split 512, "
+                         "decode + merge); one JSON line")
     ap.add_argument("--block-sweep", action="store_true",
                     help="decode time against block size (1..256), in order / scattered / "
                          "contiguous, on a 16 x 4096-token GQA batch; one JSON line per point")
@@ -963,6 +969,9 @@ def main():
         return
     if args.prefill:
         print(json.dumps(prefill_rate()), flush=True)
+        return
+    if args.gqa:
+        print(json.dumps(config_rates(only="GQA")), flush=True)
         return
     dev = torch.device("cuda:0")
     t_gen = time.time()
