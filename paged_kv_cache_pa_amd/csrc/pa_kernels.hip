@@ -348,6 +348,17 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
 #pragma unroll
     for (int g = 0; g < G; ++g)
         qv[g] = load_cached(a.q + ((qrow0 + g) * D + (int64_t)c * EPL) * sizeof(T));
+    // Append mode: the workgroup whose range ends at n takes position n - 1
+    // from k_new / v_new after the loop (wave 0), so the loop stops before it;
+    // its 16-byte pieces are requested here, with q.
+    const bool app = MODE != kDense && a.k_new != nullptr && te == n;
+    const uint32_t chunk_off = (uint32_t)(c * EPL * (int)sizeof(T));
+    vec4 kn = {}, vn = {};
+    if (app && wave == 0 && tb < te) {
+        const int64_t nsrc = ((int64_t)s * a.Hkv + h) * D * (int64_t)sizeof(T) + chunk_off;
+        kn = load_cached(a.k_new + nsrc);
+        vn = load_cached(a.v_new + nsrc);
+    }
 
     if (tb >= te) {
         // Only an empty sequence reaches here with part == 0: its row is zero.
@@ -367,7 +378,6 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
 
     // Per-lane byte offset of its 16-byte chunk of token u*R + rg of a step.
     const uint32_t tok_bytes = (uint32_t)a.tok_bytes;
-    const uint32_t chunk_off = (uint32_t)(c * EPL * (int)sizeof(T));
     uint32_t voff[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) voff[u] = (uint32_t)(u * R + rg) * tok_bytes + chunk_off;
@@ -378,9 +388,6 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     const char *kh = a.k + head0;
     const char *vh = a.v + head0;
 
-    // Append mode: the workgroup whose range ends at n takes position n - 1
-    // from k_new / v_new after the loop, so the loop stops before it.
-    const bool app = MODE != kDense && a.k_new != nullptr && te == n;
     const int le = app ? te - 1 : te;
     const int nblk = (le - tb + B - 1) >> a.log2B;
     const int chunk_blocks = MODE == kDense ? nblk : kTableChunk;
@@ -472,46 +479,49 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
             }
         };
 
-        // Full steps: wave w takes steps w, w + 4, ...  The next step's loads
-        // are always issued before the current step is computed, with no
-        // conditional loads inside the loop, so exactly one step of loads is
-        // outstanding while a step is computed.
+        // Steps: wave w takes steps w, w + 4, ... of the nst steps, the
+        // partly filled last one (index nfull, if any) included.  The next
+        // step's loads are always issued before the current step is
+        // computed, so exactly one step of loads is outstanding while a step
+        // is computed, the partly filled one too.  Only the last step of a
+        // wave can be that one: it is issued with MASKED where it can occur
+        // (a wave-uniform test) and computed with MASKED at the two places a
+        // wave's last step is computed.
+        const int nst = nfull + (tail ? 1 : 0);
+        auto issue_any = [&](vec4 (&kb)[U], vec4 (&vb)[U], int jj) {
+            if (jj < nfull)
+                issue.template operator()<false>(kb, vb, jj);
+            else
+                issue.template operator()<true>(kb, vb, jj);
+        };
+        auto compute_last = [&](const vec4 (&kb)[U], const vec4 (&vb)[U], int jj) {
+            if (jj < nfull)
+                compute.template operator()<false>(kb, vb, jj);
+            else
+                compute.template operator()<true>(kb, vb, jj);
+        };
         vec4 ka[U], va[U], kb2[U], vb2[U];
         int j = wave;
-        if (j < nfull) {
-            issue.template operator()<false>(ka, va, j);
-            while (j + 2 * nw < nfull) {
-                issue.template operator()<false>(kb2, vb2, j + nw);
+        if (j < nst) {
+            issue_any(ka, va, j);
+            while (j + 2 * nw < nst) {
+                issue.template operator()<false>(kb2, vb2, j + nw);   // j + nw < nst - nw <= nfull
                 __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
                 compute.template operator()<false>(ka, va, j);
-                issue.template operator()<false>(ka, va, j + 2 * nw);
+                issue_any(ka, va, j + 2 * nw);
                 __builtin_amdgcn_sched_barrier(0);
                 compute.template operator()<false>(kb2, vb2, j + nw);
                 j += 2 * nw;
             }
-            if (j + nw < nfull) {
-                issue.template operator()<false>(kb2, vb2, j + nw);
+            if (j + nw < nst) {
+                issue_any(kb2, vb2, j + nw);
                 __builtin_amdgcn_sched_barrier(0);
-                compute.template operator()<false>(ka, va, j);
-                compute.template operator()<false>(kb2, vb2, j + nw);
+                compute.template operator()<false>(ka, va, j);      // j < j + nw <= nfull
+                compute_last(kb2, vb2, j + nw);
             } else {
-                compute.template operator()<false>(ka, va, j);
+                compute_last(ka, va, j);
             }
         }
-        // The partly filled last step goes to the wave whose turn it is.
-        if (tail && wave == nfull % nw) {
-            issue.template operator()<true>(ka, va, nfull);
-            compute.template operator()<true>(ka, va, nfull);
-        }
-    }
-
-    // Append mode: this lane's 16-byte pieces of the newest K and V rows,
-    // issued before the row-group merge so that it hides their latency.
-    vec4 kn = {}, vn = {};
-    const int64_t nsrc = ((int64_t)s * a.Hkv + h) * D * (int64_t)sizeof(T) + chunk_off;
-    if (app && wave == 0) {
-        kn = load_cached(a.k_new + nsrc);
-        vn = load_cached(a.v_new + nsrc);
     }
 
     // Merge the R row groups of the wave (lanes rg*LPR + c, same c).
