@@ -100,3 +100,29 @@ def test_append_equals_write_then_decode(name, make, layout, partition):
     ref = oracle.decode(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, dt)
     assert_fp_close(f64(to_host(o2, dt), dt), ref, dt)
     assert same_bits(to_host(k2, dt), in_layout(kc, layout))
+
+
+def test_config2_append_as_benchmarked():
+    """The benchmark's launch at full size: the OPT-13B-shape batch (64
+    sequences, 40/40 heads, D 128, fp16), head-major pool, no split, one
+    pa_decode_append launch; every sequence's newest row comes from k_new /
+    v_new with its pool slot poisoned.  Pools bit-exact against the oracle's
+    write; every output row against the fp64 oracle on the original pool."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    p = W.config2()
+    k, v, kn, vn, slots = newest(p)
+    print("config2 append: sum n", int(p.context_lens.sum()), flush=True)
+    kd, vd = to_dev(in_layout(k, "HND"), "f16"), to_dev(in_layout(v, "HND"), "f16")
+    out = empty_out(p)
+    pa.pa_decode_append(to_dev(p.q, "f16"), to_dev(kn, "f16"), to_dev(vn, "f16"), kd, vd,
+                        to_dev(p.block_tables), to_dev(p.context_lens), p.scale, out,
+                        max_context_len=int(p.context_lens.max()), layout="HND")
+    torch.cuda.synchronize()
+    kw, vw = oracle.cache_write(kn, vn, k, v, slots, "f16")
+    assert same_bits(to_host(kd, "f16"), in_layout(kw, "HND"))
+    assert same_bits(to_host(vd, "f16"), in_layout(vw, "HND"))
+    ref = oracle.decode(p.q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, "f16")
+    assert_fp_close(f64(to_host(out, "f16"), "f16"), ref, "f16", "config2 decode_append HND")
