@@ -111,3 +111,29 @@ def test_prefill_grid_bound_larger_than_chunks():
     assert_fp_close(f64(run(p, "NHD", max_query_len=70), "f16"), ref(p), "f16")
     p2 = W.random_prefill(86, "f16", [70, 10], [5, 3], 2, 2, 64)
     assert_fp_close(f64(run(p2, "NHD", max_query_len=64), "f16"), ref(p2), "f16")
+
+
+@pytest.mark.parametrize("label,dtype,S,ctx,chunk,hq,hkv", [
+    ("OPT-13B prompt 8 x 1024", "f16", 8, 1024, 1024, 40, 40),
+    ("GQA chunk 512 after 3584", "bf16", 4, 4096, 512, 32, 8),
+])
+def test_prefill_bench_points_sampled(label, dtype, S, ctx, chunk, hq, hkv):
+    """The benchmark's two prefill launches at full size (head-major pool),
+    checked on sampled rows: row r of a chunk attends to positions 0 ..
+    ctx - chunk + r, so its exact value is the single-query result of that
+    row over a context of that position + 1, which the oracle's decode
+    gives.  Rows at tile edges and the ends of every sequence's chunk."""
+    print("case", label, flush=True)
+    p = W.random_prefill(84 + S, dtype, [ctx] * S, [chunk] * S, hq, hkv, 128)
+    got = run(p, "HND")
+    picks = sorted({0, 1, 31, 32, 63, 64, 127, 128, chunk // 2, chunk - 2, chunk - 1})
+    rows, seqs, lens = [], [], []
+    for s in range(S):
+        for r in picks:
+            rows.append(int(p.query_start[s]) + r)
+            seqs.append(s)
+            lens.append(ctx - chunk + r + 1)
+    rows, seqs = np.array(rows), np.array(seqs)
+    want = oracle.decode(p.q[rows], p.k_cache, p.v_cache, p.block_tables[seqs],
+                         np.array(lens, np.int32), p.scale, dtype)
+    assert_fp_close(f64(got[rows], dtype), want, dtype, label)
