@@ -458,8 +458,9 @@ def prefill_flops(ctx, chunk, seqs, hq, d):
 
 
 def prefill_rate(rounds=10, d=128):
-    """pa_prefill on the points above (head-major pools, block size 16):
-    median time per launch and achieved TFLOP/s against the dense 16-bit
+    """pa_prefill on the points above (head-major pools, block size 16, two
+    pool replicas): median over ``rounds`` groups of 8 back-to-back launches
+    of the time per launch, and achieved TFLOP/s against the dense 16-bit
     matrix-core peak."""
     import torch
 
@@ -489,9 +490,11 @@ def prefill_rate(rounds=10, d=128):
             pa.pa_prefill(q, k, v, table, cl, qs, 1.0 / np.sqrt(d), out, max_query_len=chunk,
                           max_context_len=ctx, layout="HND")
 
-        for i in range(2 * R):
+        for i in range(4 * R):
             f(i)
-        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        # 4 R launches back to back per event pair (the replicas cycled), so
+        # the events' own cost and the gaps between groups stay small
+        t = float(np.median([time_group(f, 4 * R, st) for _ in range(rounds)]))
         fl = prefill_flops(ctx, chunk, S, hq, d)
         res[label] = {"us": round(t * 1e6, 1), "TFLOP_s": round(fl / t / 1e12, 1),
                       "frac_of_2500": round(fl / t / 2.5e15, 4), "flops": fl}
