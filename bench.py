@@ -164,14 +164,18 @@ def time_group(fn, n, stream):
     return a.elapsed_time(b) * 1e-3 / n
 
 
-def time_graph(fn, n, rounds, stream):
-    """Median seconds per call of fn(0) .. fn(n-1) captured once into a HIP
-    graph and replayed ``rounds`` times, each replay between one event pair
-    on ``stream``.  A short launch costs the host more (Python binding and
-    runtime, ~12 us) than the GPU; a replay launches all n kernels without
-    host work in between, so this measures the GPU."""
+def time_graph(fn, n, rounds, stream, min_calls=16):
+    """Median seconds per call of fn(0) .. fn(m-1) (m = n rounded up to at
+    least ``min_calls``; callers cycle their n replicas by i % n) captured
+    once into a HIP graph and replayed ``rounds`` times, each replay between
+    one event pair on ``stream``.  A short launch costs the host more (Python
+    binding and runtime, ~12 us) than the GPU; a replay launches all m
+    kernels without host work in between, so this measures the GPU, and m
+    calls per event pair keep the events' own cost out of a short call's
+    time."""
     import torch
 
+    m = n * -(-min_calls // n)
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -181,7 +185,7 @@ def time_graph(fn, n, rounds, stream):
     stream.wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
-        for i in range(n):
+        for i in range(m):
             fn(i)
     torch.cuda.synchronize()
     g.replay()
@@ -194,7 +198,7 @@ def time_graph(fn, n, rounds, stream):
         g.replay()
         b.record(stream)
         b.synchronize()
-        ts.append(a.elapsed_time(b) * 1e-3 / n)
+        ts.append(a.elapsed_time(b) * 1e-3 / m)
     del g
     return float(np.median(ts))
 
