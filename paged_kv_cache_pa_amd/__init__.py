@@ -170,8 +170,16 @@ def _check(rc, what):
         raise PaError(rc, what)
 
 
+def _same_head_dim(q, pool, name):
+    """The kernels index q, out and the pool with one head dim: a pool whose
+    rows differ from q's would be read out of bounds, so refuse it here."""
+    if pool.shape[-1] != q.shape[-1]:
+        raise ValueError(f"head dim of {name} ({pool.shape[-1]}) differs from q's ({q.shape[-1]})")
+
+
 def _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout):
     S, Hq, D = q.shape
+    _same_head_dim(q, k_cache, "k_cache")
     NB, B, Hkv, _ = pool_dims(k_cache, layout)
     MBS = block_tables.shape[1]
     return DecodeParams(S, Hq, Hkv, D, B, MBS, NB,
@@ -273,6 +281,7 @@ def pa_decode_dense(q, k, v, context_lens, scale, out, *, max_context_len=None,
     if v.shape != k.shape or out.shape != q.shape or k.shape[0] != q.shape[0]:
         raise ValueError("shape mismatch")
     S, Hq, D = q.shape
+    _same_head_dim(q, k, "k")
     _, Smax, Hkv, _ = pool_dims(k, layout)
     p = DecodeParams(S, Hq, Hkv, D, 16, 1, 1,
                      Smax if max_context_len is None else int(max_context_len),
@@ -423,6 +432,7 @@ def pa_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, sca
     S = context_lens.shape[0]
     if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
         raise ValueError("block_tables [S, MBS], context_lens [S], query_start [S + 1]")
+    _same_head_dim(q, k_cache, "k_cache")
     NB, B, Hkv, D = pool_dims(k_cache, layout)
     MBS = block_tables.shape[1]
     rows = q.shape[0]

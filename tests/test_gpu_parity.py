@@ -411,3 +411,29 @@ def test_side_stream():
         pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=200, partition_size=64)
     s.synchronize()
     check(p, to_host(out, "f16"), ref_decode(p), "side stream")
+
+
+def test_binding_refuses_mismatched_head_dim():
+    """q and the pool must share the head dim: the binding raises before any
+    launch (decode, append, dense and prefill)."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    dev = "cuda"
+    q = torch.zeros((2, 4, 128), dtype=torch.float16, device=dev)
+    k = torch.zeros((8, 16, 4, 64), dtype=torch.float16, device=dev)
+    bt = torch.zeros((2, 4), dtype=torch.int32, device=dev)
+    cl = torch.ones((2,), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    with pytest.raises(ValueError, match="head dim"):
+        pa.pa_decode(q, k, k, bt, cl, 1.0, out)
+    kn = torch.zeros((2, 4, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(ValueError, match="head dim"):
+        pa.pa_decode_append(q, kn, kn, k, k, bt, cl, 1.0, out)
+    kd = torch.zeros((2, 32, 4, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(ValueError, match="head dim"):
+        pa.pa_decode_dense(q, kd, kd, cl, 1.0, out)
+    qs = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
+    with pytest.raises(ValueError, match="head dim"):
+        pa.pa_prefill(q, k, k, bt, cl, qs, 1.0, out)
