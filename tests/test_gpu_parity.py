@@ -386,8 +386,10 @@ def test_share_fixture_end_to_end(golden):
 
 @pytest.mark.parametrize("S", [1, 2, 255, 256, 257, 600])
 def test_batch_sizes_and_scheduling(S):
-    """Longest-first order is used up to 256 sequences, natural order above;
-    both must give every row, ties included."""
+    """Batch sizes around the 256-sequence limit of longest-first order, with
+    ties: every row must match (at these grids, 2 kv heads, at most 512
+    workgroups, so the order is the natural one; the ranked order is
+    test_longest_first_order_every_kernel's)."""
     rng = np.random.default_rng(40 + S)
     lens = rng.integers(0, 90, size=S)
     lens[::5] = 33  # many ties
@@ -395,6 +397,26 @@ def test_batch_sizes_and_scheduling(S):
     for layout in LAYOUTS:
         check(p, run_decode(p, layout=layout), ref_decode(p), f"S={S} {layout}")
     check(p, run_decode(p, partition_size=32), ref_decode(p), f"S={S} split")
+
+
+@pytest.mark.parametrize("dtype,S,hq,hkv,d", [
+    ("bf16", 200, 16, 4, 128),   # matrix-core kernel (G 4), 800 workgroups
+    ("f32", 130, 8, 4, 64),      # VALU kernel with G 2, 520 workgroups
+    ("f16", 256, 3, 3, 128),     # VALU kernel, MHA, 768 workgroups, 256 sequences
+])
+def test_longest_first_order_every_kernel(dtype, S, hq, hkv, d):
+    """Longest-first order (more than 512 workgroups, at most 256 sequences,
+    no split) in each decode kernel form, with many tied lengths, empty and
+    one-token sequences: every row must match the oracle."""
+    rng = np.random.default_rng(4000 + S)
+    lens = rng.integers(0, 120, size=S)
+    lens[::7] = 33
+    lens[3::11] = 0
+    lens[5::13] = 1
+    print("case", dtype, S, hq, hkv, d, flush=True)
+    p = W.random_paged(4100 + S, dtype, lens, hq, hkv, d, extra_blocks=2)
+    for layout in LAYOUTS:
+        check(p, run_decode(p, layout=layout), ref_decode(p), f"ranked {dtype} {layout}")
 
 
 def test_side_stream():
