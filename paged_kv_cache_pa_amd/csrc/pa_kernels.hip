@@ -224,14 +224,24 @@ __device__ int rank_pick(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, i
                          int nt_) {
     for (int t = tid; t < a.S; t += nt_) s_len[t] = clamp_len(a.lens[t], a.max_ctx);
     __syncthreads();
-    for (int t = tid; t < a.S; t += nt_) {
+    // The rank of sequence t (how many are longer, or as long with a lower
+    // index) is counted by k consecutive lanes, each over a contiguous
+    // k-th of the lengths, and summed by lane exchanges (k <= 8, k * S <=
+    // threads, so the k lanes of t share a wave and every t has its lanes).
+    int k = 1;
+    while (k < 8 && 2 * k * a.S <= nt_) k *= 2;
+    const int t = tid / k, j = tid % k;
+    if (t < a.S) {
         const int nt = s_len[t];
+        const int per = (a.S + k - 1) / k;
+        const int u0 = j * per, u1 = min(a.S, u0 + per);
         int r = 0;
-        for (int u = 0; u < a.S; ++u) {
+        for (int u = u0; u < u1; ++u) {
             const int nu = s_len[u];
             r += (nu > nt) | ((nu == nt) & (u < t));
         }
-        if (r == want) *s_pick = t;
+        for (int off = 1; off < k; off <<= 1) r += __shfl_xor(r, off, 64);
+        if (j == 0 && r == want) *s_pick = t;
     }
     __syncthreads();
     return *s_pick;
