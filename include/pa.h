@@ -15,8 +15,10 @@
  *  - Pointers named as device pointers must point to GPU memory on the
  *    current HIP device; parameter structs are host memory read during the
  *    call only.  The caller owns every buffer, including the split-K
- *    workspace.  The library allocates, frees and synchronises nothing and
- *    keeps no state between calls (reentrant).
+ *    workspace.  The library allocates, frees and synchronises nothing.
+ *    Between calls it keeps only a cache of per-device occupancy figures
+ *    (filled on first use, guarded by a lock) and, per thread, the name of
+ *    the last HIP error (pa_last_hip_error); calls are reentrant.
  *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the legacy default
  *    stream) and the call returns at once.  Buffers must stay valid until the
  *    stream has passed the work.
