@@ -633,8 +633,8 @@ def block_sweep(rounds=10, seqs=16, ctx=4096, hq=12, hkv=2, d=128, partition=256
 
 
 def sweep(rounds=10):
-    """Every configuration's kernels, timed over rotating replicas (one JSON
-    object per line; not the benchmark's contract line)."""
+    """Every configuration's kernels, timed as HIP-graph replays over rotating
+    replicas (one JSON object per line; not the benchmark's contract line)."""
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -667,7 +667,7 @@ def sweep(rounds=10):
 
         for i in range(2 * R):
             f(i)
-        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        t = time_graph(f, R, rounds, st)
         b = nbytes or decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, e, p.block_size)
         emit(config=label, kernel="pa_decode", layout=layout, partition=ps, us=round(t * 1e6, 2),
              algorithmic_bytes=b, GB_s=round(b / t / 1e9, 1), frac=round(b / t / 8e12, 4),
@@ -687,7 +687,7 @@ def sweep(rounds=10):
 
         for i in range(R):
             f(i)
-        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        t = time_graph(f, R, rounds, st)
         N = p.slot_mapping.shape[0]
         b = 2 * 2 * N * p.num_kv_heads * p.head_dim * W.ELEM_BYTES[p.dtype] + 4 * N
         emit(config=label, kernel="pa_cache_write", layout=layout, tokens=N, us=round(t * 1e6, 2),
@@ -707,7 +707,7 @@ def sweep(rounds=10):
 
         for i in range(R):
             f(i)
-        t = float(np.median([time_group(f, R, st) for _ in range(rounds)]))
+        t = time_graph(f, R, rounds, st)
         n = p.block_pairs.shape[0]
         b = 2 * 2 * n * p.block_size * p.num_kv_heads * p.head_dim * W.ELEM_BYTES[p.dtype] + 8 * n
         emit(config=label, kernel="pa_copy_blocks", pairs=n, us=round(t * 1e6, 2),
