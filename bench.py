@@ -70,6 +70,25 @@ def decode_bytes(lens, hq, hkv, d, e, block):
     return kv + qo + table + 4 * len(lens)
 
 
+def unique_decode_bytes(tables, lens, hq, hkv, d, e, block):
+    """Algorithmic bytes of one decode launch counting each physical block
+    once: a block shared by several sequences (copy-on-write sharing) is
+    stored once in HBM, so its valid rows are read from HBM at most once;
+    its valid rows are the most any sharer uses.  q, out, table and lengths
+    as in decode_bytes."""
+    tables = np.asarray(tables)
+    lens = np.asarray(lens, dtype=np.int64)
+    rows = {}
+    for s, n in enumerate(lens):
+        for j in range(int(-(-n // block))):
+            b = int(tables[s, j])
+            rows[b] = max(rows.get(b, 0), int(min(block, n - j * block)))
+    kv = sum(rows.values()) * hkv * d * 2 * e
+    qo = 2 * len(lens) * hq * d * e
+    table = 4 * int(((lens + block - 1) // block).sum())
+    return kv + qo + table + 4 * len(lens)
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -235,28 +254,78 @@ def copy_blocks_rate(rounds=15):
             "eager_us": round(te * 1e6, 2)}
 
 
-def hbm_reference(rounds=10, gib=1):
-    """Reference rates of plain PyTorch kernels on the same GPU (not this
-    library): a device-to-device copy (bytes read + written) and a sum over
-    int64 words (bytes read), each over ``gib`` GiB, so the decode and copy
-    rates can be read against what a simple streaming kernel reaches here."""
+def stream_lib():
+    """The benchmark's bandwidth reference kernels (libpa_stream.so, built
+    beside libpa.so from csrc/stream_ref.hip; not part of the library)."""
+    import ctypes
+
+    from paged_kv_cache_pa_amd.build import STREAM_LIB_PATH
+
+    if not os.path.exists(STREAM_LIB_PATH):
+        raise RuntimeError(f"{STREAM_LIB_PATH} is not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(STREAM_LIB_PATH)
+    P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.pa_ref_stream_read.argtypes = [P, SZ, I, ctypes.c_uint32, P, P]
+    L.pa_ref_stream_copy.argtypes = [P, P, SZ, I, P]
+    L.pa_ref_stream_read.restype = I
+    L.pa_ref_stream_copy.restype = I
+    L.pa_ref_threads.restype = I
+    return L
+
+
+STREAM_GRIDS = (256, 512, 1024, 2048, 4096, 8192)
+
+
+def stream_reference(nbytes, replicas=4, rounds=10):
+    """What a kernel that only moves the bytes reaches on this GPU: a plain
+    streaming read of ``nbytes`` (the decode launch's algorithmic bytes) and a
+    plain copy of ``nbytes`` / 2 each way, with the decode kernels' 16-byte
+    non-temporal loads, one contiguous chunk per workgroup.  ``replicas``
+    buffers are cycled so that no launch finds its data in the last-level
+    cache.  Every grid size in STREAM_GRIDS is timed (R back-to-back launches
+    between one event pair, median over rounds); the best is the reference."""
+    import ctypes
+
     import torch
 
+    L = stream_lib()
     st = torch.cuda.current_stream()
-    n = (gib << 30) // 8
-    src = torch.randint(0, 1 << 20, (n,), dtype=torch.int64, device="cuda")
-    dst = torch.empty_like(src)
-    acc = torch.empty((), dtype=torch.int64, device="cuda")
-    res = {}
-    for name, fn, nbytes in (("copy_GB_s", lambda i: dst.copy_(src), 2 * n * 8),
-                             ("sum_read_GB_s", lambda i: torch.sum(src, dim=0, out=acc), n * 8)):
-        fn(0)
-        t = float(np.median([time_group(fn, 1, st) for _ in range(rounds)]))
-        res[name] = round(nbytes / t / 1e9, 1)
-    del src, dst
+    sth = ctypes.c_void_p(st.cuda_stream)
+    n = -(-nbytes // 16) * 16
+    bufs = [torch.empty(n // 8, dtype=torch.int64, device="cuda").random_() for _ in range(replicas)]
+    sink = torch.zeros(L.pa_ref_threads() * 4, dtype=torch.int32, device="cuda")
+    key = int(np.random.default_rng(7).integers(1, 2**32 - 1))
+    half = -(-(n // 2) // 16) * 16
+    dsts = [torch.empty(half // 8, dtype=torch.int64, device="cuda") for _ in range(replicas)]
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed: hipError {rc}")
+
+    read, copy = {}, {}
+    for wg in STREAM_GRIDS:
+        def f_read(i, wg=wg):
+            check(L.pa_ref_stream_read(ctypes.c_void_p(bufs[i % replicas].data_ptr()), n, wg, key,
+                                       ctypes.c_void_p(sink.data_ptr()), sth), "stream read")
+
+        def f_copy(i, wg=wg):
+            check(L.pa_ref_stream_copy(ctypes.c_void_p(dsts[i % replicas].data_ptr()),
+                                       ctypes.c_void_p(bufs[i % replicas].data_ptr()), half, wg,
+                                       sth), "stream copy")
+
+        for f, res, moved in ((f_read, read, n), (f_copy, copy, 2 * half)):
+            for i in range(2 * replicas):
+                f(i)
+            t = float(np.median([time_group(f, 4 * replicas, st) for _ in range(rounds)]))
+            res[wg] = round(moved / t / 1e9, 1)
+    del bufs, dsts
     torch.cuda.empty_cache()
-    res["what"] = "torch copy_ / sum over 1 GiB of int64 on the same GPU"
-    return res
+    return {"read_GB_s": max(read.values()), "copy_GB_s": max(copy.values()),
+            "read_bytes": n, "copy_bytes_moved": 2 * half, "replicas": replicas,
+            "read_by_workgroups": read, "copy_by_workgroups": copy,
+            "what": "plain streaming read / copy kernels (csrc/stream_ref.hip): 16-byte "
+                    "non-temporal loads, one contiguous chunk per workgroup, 512 threads; "
+                    "best grid size"}
 
 
 def copy_layers_rate(rounds=10, layers=40):
@@ -550,9 +619,20 @@ def config_rates(rounds=10, only=None):
             f(i)
         t = time_graph(f, R, rounds, st)
         b = decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, W.ELEM_BYTES[p.dtype], p.block_size)
-        res[label] = {"us": round(t * 1e6, 2), "algorithmic_bytes": b,
-                      "GB_s": round(b / t / 1e9, 1), "frac_of_8000": round(b / t / 8e12, 4),
-                      "kv_tokens_per_s": round(float(p.context_lens.sum()) / t, 1), "replicas": R}
+        u = unique_decode_bytes(p.block_tables, p.context_lens, Hq, p.num_kv_heads, D,
+                                W.ELEM_BYTES[p.dtype], p.block_size)
+        r = {"us": round(t * 1e6, 2), "kv_tokens_per_s": round(float(p.context_lens.sum()) / t, 1),
+             "replicas": R}
+        if u == b:
+            r.update({"algorithmic_bytes": b, "GB_s": round(b / t / 1e9, 1),
+                      "frac_of_8000": round(b / t / 8e12, 4)})
+        else:  # blocks shared between sequences: HBM holds (and must read) each once
+            r.update({"unique_bytes": u, "GB_s": round(u / t / 1e9, 1),
+                      "frac_of_8000": round(u / t / 8e12, 4),
+                      "logical_bytes": b, "logical_GB_s": round(b / t / 1e9, 1),
+                      "bytes": "GB_s and frac_of_8000 on unique bytes (each physical block "
+                               "once); logical = every sequence's rows as it reads them"})
+        res[label] = r
         del pools, k0, v0
         torch.cuda.empty_cache()
     return res
@@ -1118,12 +1198,20 @@ def main():
     }
     if not args.no_extras:
         try:
+            ref = stream_reference(launch_bytes)
+            result["stream_reference"] = ref
+            result["roofline"]["stream_read_GB_s"] = ref["read_GB_s"]
+            result["roofline"]["frac_of_stream_read"] = round(achieved / ref["read_GB_s"], 4)
+        except Exception as e:  # report, do not lose the main line
+            result["stream_reference"] = {"error": repr(e)}
+        log("stream reference done")
+        try:
             result["other_workloads"] = config_rates()
         except Exception as e:  # report, do not lose the main line
             result["other_workloads"] = {"error": repr(e)}
         log("other workloads done")
         try:
-            result["paged_vs_dense"] = paged_dense_ratio([(8, 256), (32, 1024), (128, 2048)])
+            result["paged_vs_dense"] = paged_dense_ratio(W.CONFIG3_POINTS)
         except Exception as e:  # report, do not hide the main result
             result["paged_vs_dense"] = {"error": repr(e)}
         log("paged/dense done")
@@ -1132,8 +1220,7 @@ def main():
         except Exception as e:
             result["copy_blocks"] = {"error": repr(e)}
         log("copy_blocks done")
-        for key, fn in (("hbm_reference", hbm_reference),
-                        ("copy_blocks_layers", copy_layers_rate),
+        for key, fn in (("copy_blocks_layers", copy_layers_rate),
                         ("cache_write_layers", write_layers_rate), ("swap", swap_rate),
                         ("block_manager", block_manager_rate), ("prefill", prefill_rate)):
             try:

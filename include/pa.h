@@ -73,7 +73,8 @@ typedef enum {
     PA_ERR_DTYPE = -3,       /* dtype is not one of pa_dtype                 */
     PA_ERR_ALIGN = -4,       /* a data pointer is not 16-byte aligned        */
     PA_ERR_UNSUPPORTED = -5, /* valid but not built: head_dim not 64/128,
-                                query heads per kv head above 8, more than
+                                query heads per kv head above 8 (fp32) or
+                                16 (fp16 / bf16), more than
                                 65535 partitions or 2^31 - 1 (seq, head) rows,
                                 a token row (all kv heads) above 128 MiB      */
     PA_ERR_WORKSPACE = -6,   /* split-K workspace missing or too small       */

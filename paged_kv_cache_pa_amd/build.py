@@ -1,4 +1,6 @@
-"""Build the HIP library ``libpa.so`` in-tree for gfx950.
+"""Build the HIP library ``libpa.so`` in-tree for gfx950, and beside it
+``libpa_stream.so``, the benchmark's bandwidth reference kernels (a plain
+streaming read and copy; not part of the library's C ABI).
 
     python -m paged_kv_cache_pa_amd.build
 """
@@ -14,6 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_kernels.hip", "pa_abi.cpp", "block_manager.cpp"]
+STREAM_LIB_PATH = os.path.join(PKG, "libpa_stream.so")
+STREAM_SOURCES = ["stream_ref.hip"]
 ARCH = "gfx950"
 
 
@@ -25,13 +29,20 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp"
+    """Both libraries; returns the path of libpa.so."""
+    _build_one(SOURCES, LIB_PATH, verbose)
+    _build_one(STREAM_SOURCES, STREAM_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _build_one(sources, lib_path, verbose):
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
            # packed fp32 VALU ops stay off (no v_pk_*_f32 anywhere in this library)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-Wall", "-Wno-unused-command-line-argument",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
+    cmd += [os.path.join(CSRC, s) for s in sources]
     cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,8 +53,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":

@@ -8,13 +8,14 @@
 //          2-4x Comes From"
 //   [Res]  "Paged Attention: Managing the KV Cache Like Virtual Memory"
 //
-// Decode design (one workgroup of 4 wave64 per (sequence, kv head,
-// partition)):
+// Decode design (one workgroup of 4 or 8 wave64 per (sequence, kv head,
+// partition); the launcher picks the wave count from the kernel's occupancy,
+// see pick_waves):
 //  * A token row of one kv head is D * e bytes (256 B for fp16/bf16 D=128
 //    and fp32 D=64).  LPR = D*e/16 lanes read it with one 16-byte load each,
 //    so one wave load instruction covers R = 64/LPR whole rows and every
 //    byte fetched is used.  A wave step is 16 consecutive tokens (U = 16/R
-//    loads of K and U of V); the four waves take steps round robin and
+//    loads of K and U of V); the waves take steps round robin and
 //    issue their next step's loads before computing the current one.  K and
 //    V are streamed once, so they are read with non-temporal loads.
 //  * Two pool layouts are addressed through strides: token-major blocks
@@ -32,7 +33,7 @@
 //  * Softmax: each row group keeps its own running (max, sum, acc) in the
 //    base-2 domain (scale * log2 e folded into the score), updated once per
 //    step; the R row groups of a wave are merged with lane exchanges and the
-//    four waves through LDS at the end.  This is the one-pass form of the
+//    waves through LDS at the end.  This is the one-pass form of the
 //    [Kwon] §3.4 two-pass softmax; both equal the defining equation in exact
 //    arithmetic.  The reduction order depends only on logical token order,
 //    never on where blocks sit, so paged and dense results are bitwise equal
@@ -1840,9 +1841,11 @@ int launch_move_blocks(const BlockMove &m, int32_t n, void *stream) {
 const char *hip_error_name(int err) { return hipGetErrorName((hipError_t)err); }
 
 const char *kernel_build_info() {
-    return "gfx950; decode: 256 threads (4 wave64), 16-token wave steps, non-temporal K/V loads, "
-           "LDS block table, longest-first order up to 256 sequences, G in 1..8 (1..16 for 16-bit types), D in {64,128}, "
-           "fp32/fp16/bf16, token- or head-major blocks; cache_write / copy_blocks: 16-byte vectors";
+    return "gfx950; decode: 4 or 8 wave64 per workgroup (chosen per launch from occupancy), "
+           "16-token wave steps, non-temporal K/V loads, LDS block table, longest-first order up "
+           "to 256 sequences, G in 1..8 (1..16 for 16-bit types, on matrix cores from G 2), "
+           "D in {64,128}, fp32/fp16/bf16, token- or head-major blocks; prefill: matrix cores, "
+           "fp16/bf16; cache_write / copy_blocks: 16-byte vectors";
 }
 
 }  // namespace pa

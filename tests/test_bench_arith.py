@@ -64,3 +64,30 @@ def test_replicas_leave_the_last_level_cache():
     assert bench.replicas_for(87_000_000) * 87_000_000 >= 1 << 30
     assert bench.replicas_for(1) == 64                     # capped
     assert np.all([bench.replicas_for(b) >= 2 for b in (1, 10**6, 10**9, 10**10)])
+
+
+def test_unique_bytes_hand_count():
+    # 2 sequences sharing block 0 (16 full rows); sequence 0 also holds
+    # block 1 with 3 rows, sequence 1 block 2 with 5 rows; 1 kv head, D 8,
+    # 2-byte elements: unique K/V rows 16 + 3 + 5 = 24, logical 19 + 21 = 40
+    tables = np.array([[0, 1], [0, 2]], np.int32)
+    lens = [19, 21]
+    rest = 2 * 2 * 1 * 8 * 2 + 4 * 4 + 4 * 2          # q/out, 4 table entries, 2 lengths
+    assert bench.unique_decode_bytes(tables, lens, 1, 1, 8, 2, 16) == 24 * 8 * 2 * 2 + rest
+    assert bench.decode_bytes(lens, 1, 1, 8, 2, 16) == 40 * 8 * 2 * 2 + rest
+    # a block shared with different fill: its most-used rows count once
+    tables = np.array([[4], [4]], np.int32)
+    assert bench.unique_decode_bytes(tables, [7, 12], 1, 1, 8, 2, 16) == \
+        12 * 8 * 2 * 2 + 2 * 2 * 8 * 2 + 4 * 2 + 4 * 2
+
+
+def test_beams_unique_bytes():
+    """Parallel sampling: each group's 512-token prompt (32 full blocks) is
+    stored once and read by its 6 beams; after the copy-on-write split every
+    beam owns its stem block and suffix.  So the unique K/V rows are the
+    logical ones minus 5 x 512 per group."""
+    p = W.config4(poison=False).paged
+    e, row = 2, 40 * 128 * 2 * 2
+    logical = bench.decode_bytes(p.context_lens, 40, 40, 128, e, 16)
+    unique = bench.unique_decode_bytes(p.block_tables, p.context_lens, 40, 40, 128, e, 16)
+    assert logical - unique == 16 * 5 * 512 * row

@@ -138,13 +138,15 @@ def test_config5_gqa_split(layout):
     check(p, got0, ref, f"config5 {layout} no split")
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("n", [4096, 10000, 12000, 16384])
-def test_config5_uniform_batches(n):
+def test_config5_uniform_batches(n, layout):
+    """Every row (8 sequences x 12 query heads) of each uniform batch."""
     p = W.config5(uniform_len=n)
-    units = [(s, h) for s in (0, 7) for h in range(12)]
-    ref = ref_decode(p, units=units)
-    got = run_decode(p, partition_size=512)
-    check(p, got, ref, f"config5 uniform {n}", units=units)
+    ref = ref_decode(p)
+    t = upload(p, layout)
+    got = run_decode(p, partition_size=512, tensors=t, layout=layout)
+    check(p, got, ref, f"config5 uniform {n} {layout}")
 
 
 # ---------------------------------------------------------------- the pages' fixtures
