@@ -17,8 +17,11 @@
  *    call only.  The caller owns every buffer, including the split-K
  *    workspace.  The library allocates, frees and synchronises nothing.
  *    Between calls it keeps only a cache of per-device occupancy figures
- *    (filled on first use, guarded by a lock) and, per thread, the name of
- *    the last HIP error (pa_last_hip_error); calls are reentrant.
+ *    (filled on first use, guarded by a lock), per thread the name of the
+ *    last HIP error (pa_last_hip_error), and for pa_decode_no_alloc a fixed
+ *    16 MiB device array per device with its cached address (see there);
+ *    calls are reentrant, except that pa_decode_no_alloc calls overlapping
+ *    on one device share that array.
  *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the legacy default
  *    stream) and the call returns at once.  Buffers must stay valid until the
  *    stream has passed the work.
@@ -81,8 +84,10 @@ typedef enum {
     PA_ERR_HIP = -7,         /* the HIP launch failed                         */
     PA_ERR_NO_BLOCKS = -8,   /* block manager: the pool cannot supply the
                                 blocks a call needs (nothing was changed)    */
-    PA_ERR_STATE = -9        /* block manager: a sequence handle is not live,
+    PA_ERR_STATE = -9,       /* block manager: a sequence handle is not live,
                                 repeated, or on the wrong side for the call  */
+    PA_ERR_SCRATCH = -10     /* pa_decode_no_alloc: the split-K partials need
+                                more than PA_NO_ALLOC_SCRATCH_BYTES          */
 } pa_status;
 
 /* Shape of one decode call (host struct). */
@@ -157,6 +162,34 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               const int32_t *block_tables, const int32_t *context_lens, float scale,
               void *out, const pa_decode_params *p, void *workspace, size_t ws_bytes,
               void *stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory or pass a buffer they own: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid allocation.  The split-K
+ * partials go to a fixed array of PA_NO_ALLOC_SCRATCH_BYTES (16 MiB) that
+ * the library holds in device memory, one per device, from the library's
+ * load until the process ends.  The call allocates and frees nothing; its
+ * first call with a split on a device looks up that device's array address
+ * (hipGetSymbolAddress) and caches it.
+ *
+ * Same parameters, checks, preconditions and results as pa_decode (the same
+ * kernels, with the array as their workspace: bitwise the same output).
+ * Returns PA_ERR_SCRATCH, before any HIP call, when
+ * pa_decode_workspace_size(p) exceeds PA_NO_ALLOC_SCRATCH_BYTES (e.g. 64
+ * sequences x 40 query heads x 12 partitions x 130 x 4 bytes = 16 MB fits;
+ * 13 partitions do not).
+ *
+ * Every call on a device shares that device's array, and the array keeps
+ * the last call's partials; nothing in it needs to start at zero.  Calls
+ * whose work overlaps on one device (different streams, or other host
+ * threads) race on the array and give unspecified results: order them on
+ * one stream, or use pa_decode with a workspace of each caller's own.
+ */
+#define PA_NO_ALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pa_decode_no_alloc(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       void *out, const pa_decode_params *p, void *stream);
 
 /*
  * decode_append: the decode iteration's write and attention in one launch.

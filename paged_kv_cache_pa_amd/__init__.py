@@ -7,8 +7,8 @@ runs in the library's HIP kernels.  There is no CPU fallback: if the library
 is not built, every call raises.
 
 Entry points (same names as the C ABI):
-  pa_decode, pa_decode_append, pa_decode_dense, pa_decode_workspace_size, pa_cache_write,
-  pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
+  pa_decode, pa_decode_no_alloc, pa_decode_append, pa_decode_dense, pa_decode_workspace_size,
+  pa_cache_write, pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
 and the host block manager (``include/pa_block_manager.h``) as the class
 ``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
 """
@@ -19,7 +19,7 @@ import os
 
 from .build import LIB_PATH
 
-__all__ = ["pa_decode", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
+__all__ = ["pa_decode", "pa_decode_no_alloc", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
            "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers", "pa_swap_blocks",
            "pa_prefill", "PaError",
            "lib",
@@ -27,7 +27,11 @@ __all__ = ["pa_decode", "pa_decode_append", "pa_decode_dense", "pa_decode_worksp
 
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_DTYPE",
           -4: "PA_ERR_ALIGN", -5: "PA_ERR_UNSUPPORTED", -6: "PA_ERR_WORKSPACE",
-          -7: "PA_ERR_HIP", -8: "PA_ERR_NO_BLOCKS", -9: "PA_ERR_STATE"}
+          -7: "PA_ERR_HIP", -8: "PA_ERR_NO_BLOCKS", -9: "PA_ERR_STATE", -10: "PA_ERR_SCRATCH"}
+
+# Bytes of the fixed device array pa_decode_no_alloc uses as its workspace
+# (PA_NO_ALLOC_SCRATCH_BYTES in include/pa.h).
+NO_ALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PaError(RuntimeError):
@@ -96,6 +100,7 @@ def lib():
         DP, CP = ctypes.POINTER(DecodeParams), ctypes.POINTER(CacheParams)
         L.pa_decode_workspace_size.argtypes = [DP, ctypes.POINTER(SZ)]
         L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
+        L.pa_decode_no_alloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P]
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
         L.pa_decode_dense.argtypes = [P, P, P, P, ctypes.c_float, P, DP, I32, P, SZ, P]
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
@@ -105,7 +110,8 @@ def lib():
         L.pa_prefill.argtypes = [P, P, P, P, P, P, ctypes.c_float, P,
                                  ctypes.POINTER(PrefillParams), P]
         L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
-        for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_append", "pa_decode_dense",
+        for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_no_alloc",
+                  "pa_decode_append", "pa_decode_dense",
                   "pa_cache_write",
                   "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers",
                   "pa_swap_blocks", "pa_prefill"):
@@ -233,6 +239,31 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
     _check(lib().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
                            _ptr(ws), nbytes, _stream(stream)), "pa_decode")
+    return out
+
+
+def pa_decode_no_alloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
+                       max_context_len=None, partition_size=0, stream=None, layout="NHD"):
+    """pa_decode with no workspace: the split-K partials go to the library's
+    fixed 16 MiB device array (NO_ALLOC_SCRATCH_BYTES), so neither this call
+    nor the library allocates anything.  Calls overlapping on one device
+    share that array (order them on one stream)."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4, q.dtype)
+    _need(v_cache, "v_cache", 4, q.dtype)
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch between k_cache/v_cache or q/out")
+    if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout)
+    _check(lib().pa_decode_no_alloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                    _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
+                                    _stream(stream)), "pa_decode_no_alloc")
     return out
 
 

@@ -81,14 +81,22 @@ size_t workspace_bytes(const pa_decode_params *p) {
     return (size_t)p->num_seqs * p->num_q_heads * P * (p->head_dim + 2) * sizeof(float);
 }
 
+// Pointer checks of a decode call with at least one sequence.
+int check_decode_ptrs(const void *q, const void *k, const void *v, const int32_t *tables,
+                      const int32_t *lens, const void *out, bool dense) {
+    if (!q || !k || !v || !lens || !out || (!dense && !tables)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGN;
+    if (((uintptr_t)lens & 3u) || (tables && ((uintptr_t)tables & 3u))) return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
 int run_decode(const void *q, const void *k, const void *v, const int32_t *tables,
                const int32_t *lens, float scale, void *out, const pa_decode_params *p,
                void *ws, size_t ws_bytes, void *stream, bool dense, int32_t max_seq_len,
                const void *k_new = nullptr, const void *v_new = nullptr) {
     if (p->num_seqs == 0) return PA_OK;
-    if (!q || !k || !v || !lens || !out || (!dense && !tables)) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PA_ERR_ALIGN;
-    if (((uintptr_t)lens & 3u) || (tables && ((uintptr_t)tables & 3u))) return PA_ERR_ALIGN;
+    const int pst = check_decode_ptrs(q, k, v, tables, lens, out, dense);
+    if (pst != PA_OK) return pst;
     const size_t need = workspace_bytes(p);
     if (need) {
         if (!ws || ws_bytes < need) return PA_ERR_WORKSPACE;
@@ -201,6 +209,28 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
     if (st != PA_OK) return st;
     return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
                       ws_bytes, stream, false, 0);
+}
+
+static_assert(PA_NO_ALLOC_SCRATCH_BYTES == pa::kNoAllocScratchBytes,
+              "the header states the scratch array's size");
+
+int pa_decode_no_alloc(const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, const int32_t *context_lens, float scale,
+                       void *out, const pa_decode_params *p, void *stream) {
+    const int st = check_paged_shape(p);
+    if (st != PA_OK) return st;
+    if (p->num_seqs == 0) return PA_OK;
+    const int pst = check_decode_ptrs(q, k_cache, v_cache, block_tables, context_lens, out, false);
+    if (pst != PA_OK) return pst;
+    const size_t need = workspace_bytes(p);
+    if (need > PA_NO_ALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (need) {  // every check has passed: the first HIP call
+        const int e = pa::scratch_address(&ws);
+        if (e) return hip_status(e);
+    }
+    return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, ws,
+                      need ? PA_NO_ALLOC_SCRATCH_BYTES : 0, stream, false, 0);
 }
 
 int pa_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache,
@@ -367,6 +397,9 @@ const char *pa_status_string(int status) {
         case PA_ERR_HIP: return "PA_ERR_HIP: the HIP launch failed";
         case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: the block pool cannot supply the call";
         case PA_ERR_STATE: return "PA_ERR_STATE: sequence handle not live, repeated or on the wrong side";
+        case PA_ERR_SCRATCH:
+            return "PA_ERR_SCRATCH: the split-K partials need more than the fixed scratch array "
+                   "of pa_decode_no_alloc holds (PA_NO_ALLOC_SCRATCH_BYTES)";
     }
     return "unknown pa_status";
 }

@@ -1838,6 +1838,36 @@ int launch_move_blocks(const BlockMove &m, int32_t n, void *stream) {
     return (int)hipGetLastError();
 }
 
+// ---------------------------------------------------------------- static scratch
+
+// The split-K workspace of pa_decode_no_alloc: a fixed device array in place
+// of a caller-provided buffer, for callers that cannot allocate.  Every
+// device the library runs on holds its own copy at its own address until the
+// process ends.  In host code the name is only a stand-in for the symbol:
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+int scratch_address(void **ptr) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+        if (e != hipSuccess) return (int)e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
+}
+
 const char *hip_error_name(int err) { return hipGetErrorName((hipError_t)err); }
 
 const char *kernel_build_info() {

@@ -84,6 +84,14 @@ struct BlockMove {
 
 int launch_move_blocks(const BlockMove &m, int32_t n, void *stream);
 
+// Bytes of the fixed device array that serves pa_decode_no_alloc as its
+// split-K workspace (one array per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+
+// Device address of that array on the current device (looked up once per
+// device, then cached).  Returns 0, or the hipError_t of the lookup.
+int scratch_address(void **ptr);
+
 const char *hip_error_name(int err);
 const char *kernel_build_info();
 

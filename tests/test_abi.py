@@ -335,3 +335,43 @@ def test_one_hip_runtime_per_process():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1"
+
+
+def test_decode_no_alloc_checks(L):
+    """pa_decode_no_alloc validates like pa_decode and refuses a split whose
+    partials exceed its fixed scratch array, all before any HIP call."""
+    SCRATCH = -10
+    assert pa.STATUS[SCRATCH] == "PA_ERR_SCRATCH"
+    assert pa.NO_ALLOC_SCRATCH_BYTES == 16 << 20
+    b = Buf()
+
+    def call(p, *ptrs):
+        args = list(ptrs) if ptrs else [b.p] * 6
+        return L.pa_decode_no_alloc(*args[:5], ctypes.c_float(0.125), args[5],
+                                    None if p is None else ctypes.byref(p), None)
+
+    assert call(None) == NULL
+    assert call(params(dtype=7)) == DTYPE
+    assert call(params(partition_size=24)) == SHAPE       # not a multiple of the block size
+    assert call(params(head_dim=96)) == UNSUP
+    assert call(params(num_seqs=0)) == OK                 # nothing to do, nothing launched
+    for i in range(6):
+        args = [b.p] * 6
+        args[i] = None
+        assert call(params(), *args) == NULL
+    for i in (0, 1, 2, 5):
+        args = [b.p] * 6
+        args[i] = b.odd
+        assert call(params(), *args) == ALIGN
+    # 64 sequences x 40 query heads x (D 128 + 2) x 4 bytes per partition:
+    # 12 partitions fit in 16 MiB, 13 do not
+    fits = params(num_seqs=64, num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
+                  max_blocks_per_seq=128, num_blocks=2048, max_context_len=12 * 128,
+                  partition_size=128, dtype=1)
+    assert pa.pa_decode_workspace_size(fits) == 64 * 40 * 12 * 130 * 4 <= pa.NO_ALLOC_SCRATCH_BYTES
+    over = params(num_seqs=64, num_q_heads=40, num_kv_heads=40, head_dim=128, block_size=16,
+                  max_blocks_per_seq=128, num_blocks=2048, max_context_len=13 * 128,
+                  partition_size=128, dtype=1)
+    assert pa.pa_decode_workspace_size(over) > pa.NO_ALLOC_SCRATCH_BYTES
+    assert call(over) == SCRATCH
+    assert b"scratch" in L.pa_status_string(SCRATCH)
