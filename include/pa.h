@@ -123,7 +123,7 @@ typedef struct {
  * Bytes of workspace pa_decode / pa_decode_dense need for ``p``: zero when
  * partition_size == 0 or max_context_len <= partition_size, otherwise
  * num_seqs * num_q_heads * ceil(max_context_len / partition_size)
- * * (head_dim + 2) * 4.  Only the fields the size depends on are checked
+ * * (head_dim + 2) * 4 (fp32 partials).  Only the fields the size depends on are checked
  * (dtype, the head counts, head_dim, num_seqs, max_context_len >= 0,
  * partition_size >= 0); block_size, max_blocks_per_seq and num_blocks are
  * not read.  Writes the size to *bytes (0 on error); returns a pa_status.
@@ -150,12 +150,15 @@ int pa_decode_workspace_size(const pa_decode_params *p, size_t *bytes);
  * workspace: device pointer (16-byte aligned) to at least
  * pa_decode_workspace_size() bytes when that size is non-zero (may be NULL
  * otherwise); its contents on entry do not matter and are left unspecified.
+ * With a split, each partition stores its unnormalised partial there and a
+ * second kernel on the same stream (the merge) combines them by the
+ * log-sum-exp identity.  Calls that share a workspace must not overlap
+ * (order them on one stream).
  * Device-side conditions: 0 <= context_lens[s] <= max_context_len and
  * 0 <= block_tables[s][j] < num_blocks for j < ceil(n / B).  A longer
  * context is clamped to max_context_len (and to MBS * B); a table entry
  * outside [0, NB) is clamped into it.
- * With partition_size > 0 a second kernel (the merge) runs on the same
- * stream.  Results are bitwise deterministic for fixed inputs and launch
+ * Results are bitwise deterministic for fixed inputs and launch
  * configuration, and independent of where the blocks sit in the pool.
  */
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,

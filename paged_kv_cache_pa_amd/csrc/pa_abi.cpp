@@ -54,12 +54,24 @@ int check_decode_shape(const pa_decode_params *p, int64_t row_limit, int32_t gra
     // In-step row offsets are 32-bit: 16 token rows must span under 4 GiB.
     if ((int64_t)p->num_kv_heads * p->head_dim * elem_bytes(p->dtype) > (1 << 27))
         return PA_ERR_UNSUPPORTED;
-    // Grid x is num_seqs * num_kv_heads (the merge uses num_seqs * num_q_heads)
-    // and must fit 31 bits; grid y is the partition count.
+    // (sequence, head) rows are indexed with 31 bits.  The decode grid is one
+    // workgroup (of up to 512 threads) per (sequence, kv head, partition), the
+    // merge grid one of 256 threads per (sequence, query head); a launch's
+    // thread count must fit 32 bits.
     if ((int64_t)p->num_seqs * p->num_q_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     if (p->partition_size &&
         ((int64_t)p->max_context_len + p->partition_size - 1) / p->partition_size > 65535)
         return PA_ERR_UNSUPPORTED;
+    {
+        const int64_t parts = p->partition_size && p->max_context_len > p->partition_size
+                                  ? ((int64_t)p->max_context_len + p->partition_size - 1) /
+                                        p->partition_size
+                                  : 1;
+        if ((int64_t)p->num_seqs * p->num_kv_heads * parts * 512 > 0xFFFFFFFFll)
+            return PA_ERR_UNSUPPORTED;
+        if (parts > 1 && (int64_t)p->num_seqs * p->num_q_heads * 256 > 0xFFFFFFFFll)
+            return PA_ERR_UNSUPPORTED;
+    }
     return PA_OK;
 }
 
@@ -75,6 +87,7 @@ int32_t num_partitions(const pa_decode_params *p) {
     return (p->max_context_len + p->partition_size - 1) / p->partition_size;
 }
 
+// Partials [S, Hq, P, D] and (m, l) [S, Hq, P, 2] in fp32.
 size_t workspace_bytes(const pa_decode_params *p) {
     const int32_t P = num_partitions(p);
     if (P <= 1) return 0;

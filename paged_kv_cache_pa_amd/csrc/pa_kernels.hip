@@ -291,13 +291,25 @@ __device__ __forceinline__ void append_store(const DecodeArgs &a, const int32_t 
     *reinterpret_cast<vec4 *>(a.v_w + dst) = vn;
 }
 
+// Position of a workgroup in the one-dimensional decode grid: item = (sequence
+// slot, kv head) pair, part = its context partition.  The partitions of one
+// item take consecutive workgroup ids, and the dispatcher deals consecutive
+// ids to the eight XCDs in turn, so every item's partitions are spread over
+// all XCDs (with the partition as the slow index, each item's whole context
+// landed on one XCD and the XCDs' loads differed up to 2x on mixed lengths).
+__device__ __forceinline__ void grid_pos(const DecodeArgs &a, int &item, int &part) {
+    const int wg = (int)blockIdx.x;
+    part = a.P > 1 ? wg % a.P : 0;
+    item = a.P > 1 ? wg / a.P : wg;
+}
+
 // Which sequence a workgroup serves.  Without ranking, the first table chunk
 // does not depend on the context length, so it is fetched together with the
 // length instead of after it (*staged = true; a barrier publishes it).
 template <int MODE>
 __device__ void pick_work(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, int32_t *s_tab,
-                          int tid, int nt_, int &s, int &n, bool &staged) {
-    const int want = blockIdx.x / a.Hkv;
+                          int item, int part, int tid, int nt_, int &s, int &n, bool &staged) {
+    const int want = item / a.Hkv;
     staged = false;
     if (a.rank) {
         s = rank_pick(a, s_len, s_pick, want, tid, nt_);
@@ -306,12 +318,47 @@ __device__ void pick_work(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, 
     }
     s = want;
     if constexpr (MODE != kDense) {
-        const int b0 = (a.PS ? (int)blockIdx.y * a.PS : 0) >> a.log2B;
+        const int b0 = (a.PS ? part * a.PS : 0) >> a.log2B;
         const int cnt = min(min(kTableChunk, a.spec_blocks), a.MBS - b0);
         stage_table(a.tables + (int64_t)s * a.MBS, b0, cnt, a.NB, s_tab, tid, nt_);
         staged = true;
     }
     n = clamp_len(a.lens[s], a.max_ctx);
+}
+
+// End of a decode workgroup: combine the waves' running states (red[w][g] =
+// acc[0..D), m, l) and store either the output row (a single partition
+// covers the sequence) or the partition's unnormalised partial, which the
+// merge kernel combines.
+template <typename T, int D, int G>
+__device__ void finish_workgroup(const DecodeArgs &a, const float *red, int nw, int64_t qrow0,
+                                 int part, int n, int tid, int nthr) {
+    const bool direct = a.PS == 0 || n <= a.PS;
+    for (int i = tid; i < G * D; i += nthr) {
+        const int g = i / D, d = i % D;
+        float M = kNegBig;
+#pragma unroll
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, red[(w * G + g) * (D + 2) + D]);
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int w = 0; w < nw; ++w) {
+            const float *r = red + (w * G + g) * (D + 2);
+            const float cw = fexp2(r[D] - M);
+            L = fmaf(r[D + 1], cw, L);
+            A = fmaf(r[d], cw, A);
+        }
+        const int64_t qh = qrow0 + g;
+        if (direct) {
+            Elem<T>::store(a.out, qh * D + d, A / L);
+        } else {
+            const int64_t pi = qh * a.P + part;
+            a.ws_acc[pi * D + d] = A;
+            if (d == 0) {
+                a.ws_ml[pi * 2] = M;
+                a.ws_ml[pi * 2 + 1] = L;
+            }
+        }
+    }
 }
 
 // fp32 rows need twice the registers per token, so fp32 workgroups keep 4 waves.
@@ -343,12 +390,13 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int rg = lane / LPR;   // row group
     const int c = lane % LPR;    // 16-byte chunk of the row
-    const int h = blockIdx.x % a.Hkv;
-    const int part = blockIdx.y;
+    int item, part;
+    grid_pos(a, item, part);
+    const int h = item % a.Hkv;
 
     int s, n;
     bool staged;
-    pick_work<MODE>(a, s_len, &s_pick, s_tab, tid, nthr, s, n, staged);
+    pick_work<MODE>(a, s_len, &s_pick, s_tab, item, part, tid, nthr, s, n, staged);
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;  // first query head of the group
@@ -590,34 +638,7 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
         }
     }
     __syncthreads();
-    // A sequence that fits one partition is finished here; the merge kernel
-    // skips it.
-    const bool direct = a.PS == 0 || n <= a.PS;
-    for (int i = tid; i < G * D; i += nthr) {
-        const int g = i / D, d = i % D;
-        float M = kNegBig;
-#pragma unroll
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, red[(w * G + g) * (D + 2) + D]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int w = 0; w < nw; ++w) {
-            const float *r = red + (w * G + g) * (D + 2);
-            const float cw = fexp2(r[D] - M);
-            L = fmaf(r[D + 1], cw, L);
-            A = fmaf(r[d], cw, A);
-        }
-        const int64_t qh = qrow0 + g;
-        if (direct) {
-            E::store(a.out, qh * D + d, A / L);
-        } else {
-            const int64_t pi = qh * a.P + part;
-            a.ws_acc[pi * D + d] = A;
-            if (d == 0) {
-                a.ws_ml[pi * 2] = M;
-                a.ws_ml[pi * 2 + 1] = L;
-            }
-        }
-    }
+    finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
 }
 
 // ---------------------------------------------------------------- grouped-query decode on MFMA
@@ -753,14 +774,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tok = lane & 15;   // token of the step this lane loads; head of its score column
     const int kb = lane >> 4;    // k-block: 8 dims of each 32-dim slice; 4 tokens of the score tile
-    const int h = blockIdx.x % a.Hkv;
-    const int part = blockIdx.y;
+    int item, part;
+    grid_pos(a, item, part);
+    const int h = item % a.Hkv;
     char *ktile = smem + TAB_BYTES + wave * 2 * TILE;
     char *vtile = ktile + TILE;
 
     int s, n;
     bool staged;
-    pick_work<MODE>(a, s_len, &s_pick, s_tab, tid, nthr, s, n, staged);
+    pick_work<MODE>(a, s_len, &s_pick, s_tab, item, part, tid, nthr, s, n, staged);
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;
@@ -964,32 +986,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
         }
     }
     __syncthreads();
-    const bool direct = a.PS == 0 || n <= a.PS;
-    for (int i = tid; i < G * D; i += nthr) {
-        const int g = i / D, d = i % D;
-        float Mx = kNegBig;
-#pragma unroll
-        for (int w = 0; w < nw; ++w) Mx = fmaxf(Mx, red[(w * G + g) * (D + 2) + D]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int w = 0; w < nw; ++w) {
-            const float *r = red + (w * G + g) * (D + 2);
-            const float cw = fexp2(r[D] - Mx);
-            L = fmaf(r[D + 1], cw, L);
-            A = fmaf(r[d], cw, A);
-        }
-        const int64_t qh = qrow0 + g;
-        if (direct) {
-            E::store(a.out, qh * D + d, A / L);
-        } else {
-            const int64_t pi = qh * a.P + part;
-            a.ws_acc[pi * D + d] = A;
-            if (d == 0) {
-                a.ws_ml[pi * 2] = Mx;
-                a.ws_ml[pi * 2 + 1] = L;
-            }
-        }
-    }
+    finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
 }
 
 // Combines the partitions of one (sequence, query head): with M the largest
@@ -1205,8 +1202,8 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     }
     a.blk_bytes = l.dense ? 0 : row * l.Hkv * B;
     a.seq_bytes = l.dense ? row * l.Hkv * l.pos_stride : 0;
-    dim3 grid((unsigned)((int64_t)l.S * l.Hkv), (unsigned)l.P, 1);
     const int64_t wgs = (int64_t)l.S * l.Hkv * l.P;
+    dim3 grid((unsigned)wgs, 1, 1);
     auto red_bytes = [](int nw) { return (size_t)nw * G * (D + 2) * 4; };
     auto max2 = [](size_t x, size_t y) { return x > y ? x : y; };
     using Kern = void (*)(DecodeArgs);

@@ -375,3 +375,14 @@ def test_decode_no_alloc_checks(L):
     assert pa.pa_decode_workspace_size(over) > pa.NO_ALLOC_SCRATCH_BYTES
     assert call(over) == SCRATCH
     assert b"scratch" in L.pa_status_string(SCRATCH)
+
+
+def test_grid_thread_count_fits_32_bits(L):
+    """One workgroup of up to 512 threads per (sequence, kv head, partition):
+    a launch whose thread count would pass 2^32 is refused."""
+    p = params(num_seqs=65536, num_q_heads=128, num_kv_heads=128, head_dim=128,
+               max_blocks_per_seq=1, block_size=16, max_context_len=16, num_blocks=64)
+    assert decode(L, p) == UNSUP                       # 2^23 workgroups x 512 threads = 2^32
+    p = params(num_seqs=65535, num_q_heads=128, num_kv_heads=128, head_dim=128,
+               max_blocks_per_seq=1, block_size=16, max_context_len=16, num_blocks=64)
+    assert L.pa_decode_workspace_size(ctypes.byref(p), ctypes.byref(ctypes.c_size_t())) == OK
