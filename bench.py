@@ -265,7 +265,7 @@ def stream_lib():
         raise RuntimeError(f"{STREAM_LIB_PATH} is not built (run __graft_entry__.build())")
     L = ctypes.CDLL(STREAM_LIB_PATH)
     P, SZ, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    L.pa_ref_stream_read.argtypes = [P, SZ, I, ctypes.c_uint32, P, P]
+    L.pa_ref_stream_read.argtypes = [P, SZ, I, I, ctypes.c_uint32, P, P]
     L.pa_ref_stream_copy.argtypes = [P, P, SZ, I, P]
     L.pa_ref_stream_read.restype = I
     L.pa_ref_stream_copy.restype = I
@@ -273,17 +273,22 @@ def stream_lib():
     return L
 
 
-STREAM_GRIDS = (256, 512, 1024, 2048, 4096, 8192)
+# (access order, workgroups) of the read reference: 0 = a contiguous chunk per
+# workgroup, 1 = grid-stride
+STREAM_READ_SHAPES = [(0, w) for w in (256, 1024, 4096, 8192, 16384)] + \
+    [(1, w) for w in (256, 512, 1024, 2048, 4096)]
+STREAM_COPY_GRIDS = (1024, 4096, 8192, 16384)
 
 
 def stream_reference(nbytes, replicas=4, rounds=10):
     """What a kernel that only moves the bytes reaches on this GPU: a plain
     streaming read of ``nbytes`` (the decode launch's algorithmic bytes) and a
     plain copy of ``nbytes`` / 2 each way, with the decode kernels' 16-byte
-    non-temporal loads, one contiguous chunk per workgroup.  ``replicas``
-    buffers are cycled so that no launch finds its data in the last-level
-    cache.  Every grid size in STREAM_GRIDS is timed (R back-to-back launches
-    between one event pair, median over rounds); the best is the reference."""
+    non-temporal loads.  ``replicas`` buffers are cycled so that no launch
+    finds its data in the last-level cache.  Every access order and grid
+    size in STREAM_READ_SHAPES / STREAM_COPY_GRIDS is timed (4R back-to-back
+    launches between one event pair, median over rounds); the best is the
+    reference."""
     import ctypes
 
     import torch
@@ -302,30 +307,35 @@ def stream_reference(nbytes, replicas=4, rounds=10):
         if rc != 0:
             raise RuntimeError(f"{what} failed: hipError {rc}")
 
-    read, copy = {}, {}
-    for wg in STREAM_GRIDS:
-        def f_read(i, wg=wg):
-            check(L.pa_ref_stream_read(ctypes.c_void_p(bufs[i % replicas].data_ptr()), n, wg, key,
-                                       ctypes.c_void_p(sink.data_ptr()), sth), "stream read")
+    def timed(f, moved):
+        for i in range(2 * replicas):
+            f(i)
+        t = float(np.median([time_group(f, 4 * replicas, st) for _ in range(rounds)]))
+        return round(moved / t / 1e9, 1)
 
+    read, copy = {}, {}
+    for order, wg in STREAM_READ_SHAPES:
+        def f_read(i, wg=wg, order=order):
+            check(L.pa_ref_stream_read(ctypes.c_void_p(bufs[i % replicas].data_ptr()), n, wg,
+                                       order, key, ctypes.c_void_p(sink.data_ptr()), sth),
+                  "stream read")
+
+        read[("chunk " if order == 0 else "stride ") + str(wg)] = timed(f_read, n)
+    for wg in STREAM_COPY_GRIDS:
         def f_copy(i, wg=wg):
             check(L.pa_ref_stream_copy(ctypes.c_void_p(dsts[i % replicas].data_ptr()),
                                        ctypes.c_void_p(bufs[i % replicas].data_ptr()), half, wg,
                                        sth), "stream copy")
 
-        for f, res, moved in ((f_read, read, n), (f_copy, copy, 2 * half)):
-            for i in range(2 * replicas):
-                f(i)
-            t = float(np.median([time_group(f, 4 * replicas, st) for _ in range(rounds)]))
-            res[wg] = round(moved / t / 1e9, 1)
+        copy[wg] = timed(f_copy, 2 * half)
     del bufs, dsts
     torch.cuda.empty_cache()
     return {"read_GB_s": max(read.values()), "copy_GB_s": max(copy.values()),
             "read_bytes": n, "copy_bytes_moved": 2 * half, "replicas": replicas,
             "read_by_workgroups": read, "copy_by_workgroups": copy,
             "what": "plain streaming read / copy kernels (csrc/stream_ref.hip): 16-byte "
-                    "non-temporal loads, one contiguous chunk per workgroup, 512 threads; "
-                    "best grid size"}
+                    "non-temporal loads, a contiguous chunk per workgroup (512 threads) or "
+                    "grid-stride (256 threads); best access order and grid size"}
 
 
 def copy_layers_rate(rounds=10, layers=40):
