@@ -1415,6 +1415,16 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
             qb[c][i] = r < rows ? load_cached(a.q + (qrow * D + 32 * i + 8 * kb) * 2)
                                 : vec4{0u, 0u, 0u, 0u};
     }
+    // Scores stay in raw units (q.k) and the scale enters once per weight:
+    // p = 2^(s (x - m)) = 2^(fma(s, x, -s m)) with s = |scale| log2 e > 0.  A
+    // negative scale is moved onto q, whose sign flip is exact.
+    const float sc_abs = fabsf(a.qk_scale);
+    if (a.qk_scale < 0.0f) {
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+#pragma unroll
+            for (int i = 0; i < KL; ++i) qb[c][i] ^= vec4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
     // The q loads complete here: a wait for them must not fall inside the key
     // loop, where it would also wait for the LDS DMA in flight.
 #pragma unroll
@@ -1422,13 +1432,21 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
 #pragma unroll
         for (int i = 0; i < KL; ++i) asm volatile("" ::"v"(qb[c][i]));
 
-    float m[NQ];
+    // Running max m (raw units) per query column, and the two values derived
+    // from it that the loop uses: thr = m + 2^kLazy-in-raw-units (a score
+    // above it moves the max) and nms = -s m.  The start value is finite and
+    // far below any score, so -s m stays finite.
+    constexpr float kRawStart = -1.0e30f;
+    const float lazy_raw = kLazy / sc_abs;
+    float m[NQ], thr[NQ], nms[NQ];
     float4_t acc[NQ][DS], accl[NQ];
     const vec4 ones = M::ones();
     const int mask_free_rows = n - rows + r0;  // keys up to here are visible to every row
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
-        m[c] = kNegBig;
+        m[c] = kRawStart;
+        thr[c] = kRawStart + lazy_raw;
+        nms[c] = -sc_abs * kRawStart;
         accl[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int d = 0; d < DS; ++d) acc[c][d] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -1449,6 +1467,17 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
     const int B = 1 << a.log2B;
     const int32_t *trow = a.tables + (int64_t)s * a.MBS;
     const int64_t head0 = (int64_t)g * a.head_bytes;
+    // Scalar DMA addressing needs an instruction's rows inside one block; a
+    // lane's offset from the instruction's first row then fits 32 bits (RPI
+    // rows of at most 128 MiB each) and does not change from tile to tile.
+    const bool fast_dma = B >= RPI;
+    uint32_t lane_off[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = (wave * NI + i) * RPI + lane / CPR;
+        lane_off[i] = (uint32_t)(lane / CPR) * (uint32_t)a.tok_bytes +
+                      ((uint32_t)((lane % CPR) ^ row_swz<D>(r)) << 4);
+    }
     const int nblk = (nkeys + B - 1) >> a.log2B;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&s_kv[0][0][0];
 
@@ -1466,15 +1495,39 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
         // reload its last key) into stage st: instruction ins of the tile
         // fills rows ins * RPI .. + RPI - 1; lane l the piece at position
         // l % CPR of its row, i.e. global piece (l % CPR) ^ swz(row).
-        // The table entries are all read before the first DMA: the DMA's asm
-        // orders memory, so a read placed after one would wait for it.
+        // When the whole tile lies inside the chunk and an instruction's RPI
+        // rows lie in one block (block size >= RPI, rows RPI-aligned), the
+        // block id and the block's base are wave-uniform (scalar registers)
+        // and a lane adds only its loop-invariant row and piece offset.
+        // Otherwise every lane translates its own row.  The table entries
+        // are all read before the first DMA: the DMA's asm orders memory, so
+        // a read placed after one would wait for it.
         auto issue = [&](int j, int st) {
+            const int tt0 = ck0 + KT * j;  // first key of tile j
+            if (fast_dma && tt0 + KT <= ck1) {
+                int64_t base[NI];
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int t = tt0 + (wave * NI + i) * RPI;  // first row of the instruction
+                    const int blk = __builtin_amdgcn_readfirstlane(s_tab[(t - ck0) >> a.log2B]);
+                    base[i] = (int64_t)blk * a.blk_bytes + (int64_t)(t & (B - 1)) * a.tok_bytes + head0;
+                }
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int ins = wave * NI + i;
+                    const uint32_t dk = lds0 + (uint32_t)((st * 2 + 0) * TILEB + ins * 1024);
+                    const uint32_t dv = lds0 + (uint32_t)((st * 2 + 1) * TILEB + ins * 1024);
+                    lds_dma16(a.k + base[i] + lane_off[i], __builtin_amdgcn_readfirstlane(dk));
+                    lds_dma16(a.v + base[i] + lane_off[i], __builtin_amdgcn_readfirstlane(dv));
+                }
+                return;
+            }
             int64_t off[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int ins = wave * NI + i;
                 const int r = ins * RPI + lane / CPR;
-                int t = ck0 + KT * j + r;
+                int t = tt0 + r;
                 t = t < ck1 ? t : ck1 - 1;
                 off[i] = (int64_t)s_tab[(t - ck0) >> a.log2B] * a.blk_bytes +
                          (int64_t)(t & (B - 1)) * a.tok_bytes + head0 +
@@ -1495,7 +1548,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
         auto pair = [&](int st, int u, int key0) {
             const char *kt = &s_kv[st][0][0] + 16 * u * ROWB;
             const char *vt = &s_kv[st][1][0] + 16 * u * ROWB;
-            const bool two = key0 + 16 <= w_last;  // wave-uniform
             // A operand of O^T += V^T P^T over 32 keys: lane l holds keys
             // 4 kb .. 4 kb + 3 of both sub-tiles (k-slots 8 kb .. 8 kb + 7)
             vec4 va[DS];
@@ -1508,8 +1560,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                 const vec2 l2 = __builtin_bit_cast(vec2, lo), h2 = __builtin_bit_cast(vec2, hi);
                 va[d] = vec4{l2.x, l2.y, h2.x, h2.y};
             }
-            float x[2][NQ][4];
-            bool grow = false;
             const bool masked = key0 + 31 > mask_free;  // wave-uniform
             // K operands of both sub-tiles, requested together (the second
             // sub-tile's rows are in LDS whether or not they are used)
@@ -1519,24 +1569,34 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
 #pragma unroll
                 for (int i = 0; i < KL; ++i)
                     ka2[hh][i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
+            // The four score chains (2 sub-tiles x NQ column tiles) advance
+            // together, so consecutive products never depend on each other.
+            float4_t sc[2][NQ];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                if (hh == 1 && !two) {
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int c = 0; c < NQ; ++c)
+                for (int c = 0; c < NQ; ++c) sc[hh][c] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) x[1][c][jj] = -__builtin_inff();
-                    break;
-                }
-                const vec4 *ka = ka2[hh];
+            for (int i = 0; i < KL; ++i)
 #pragma unroll
-                for (int c = 0; c < NQ; ++c) {
-                    float4_t sc = {0.f, 0.f, 0.f, 0.f};
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int i = 0; i < KL; ++i) sc = M::qk(ka[i], qb[c][i], sc);
+                    for (int c = 0; c < NQ; ++c) sc[hh][c] = M::qk(ka2[hh][i], qb[c][i], sc[hh][c]);
+            // Keys past the wave's last row (all of the second sub-tile when
+            // key0 + 16 > w_last) are hidden by the causal mask below, which
+            // applies whenever that holds (mask_free <= w_last).
+            float x[2][NQ][4];
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) x[hh][c][jj] = sc[jj] * a.qk_scale;
-                    if (masked) {
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int c = 0; c < NQ; ++c)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) x[hh][c][jj] = sc[hh][c][jj];
+            if (masked) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int c = 0; c < NQ; ++c) {
                         // keys key0 + 16 hh + 4 kb + jj with jj > lim are hidden
                         // (causal, or past the chunk's end)
                         const int lim = min(my_pos[c], ck1 - 1) - (key0 + 16 * hh + 4 * kb);
@@ -1544,21 +1604,26 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                         for (int jj = 0; jj < 4; ++jj)
                             x[hh][c][jj] = jj > lim ? -__builtin_inff() : x[hh][c][jj];
                     }
-                    const float mx = fmaxf(fmaxf(x[hh][c][0], x[hh][c][1]),
-                                           fmaxf(x[hh][c][2], x[hh][c][3]));
-                    grow |= mx > m[c] + kLazy;
-                }
+            }
+            bool grow = false;
+            float mxc[NQ];
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                mxc[c] = fmaxf(fmaxf(fmaxf(x[0][c][0], x[0][c][1]), fmaxf(x[0][c][2], x[0][c][3])),
+                               fmaxf(fmaxf(x[1][c][0], x[1][c][1]), fmaxf(x[1][c][2], x[1][c][3])));
+                grow |= mxc[c] > thr[c];
             }
             if (__any(grow)) {
 #pragma unroll
                 for (int c = 0; c < NQ; ++c) {
-                    float mx = fmaxf(fmaxf(fmaxf(x[0][c][0], x[0][c][1]), fmaxf(x[0][c][2], x[0][c][3])),
-                                     fmaxf(fmaxf(x[1][c][0], x[1][c][1]), fmaxf(x[1][c][2], x[1][c][3])));
+                    float mx = mxc[c];
                     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                     const float mn = fmaxf(m[c], mx);
-                    const float alpha = fexp2(m[c] - mn);
+                    const float alpha = fexp2(fmaf(sc_abs, m[c], -sc_abs * mn));
                     m[c] = mn;
+                    thr[c] = mn + lazy_raw;
+                    nms[c] = -sc_abs * mn;
                     accl[c] = accl[c] * alpha;
 #pragma unroll
                     for (int d = 0; d < DS; ++d) acc[c][d] = acc[c][d] * alpha;
@@ -1571,7 +1636,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) p[hh][jj] = fexp2(x[hh][c][jj] - m[c]);
+                    for (int jj = 0; jj < 4; ++jj) p[hh][jj] = fexp2(fmaf(sc_abs, x[hh][c][jj], nms[c]));
                 const vec2 b0 = M::pack(p[0][0], p[0][1], p[0][2], p[0][3]);
                 const vec2 b1 = M::pack(p[1][0], p[1][1], p[1][2], p[1][3]);
                 pb[c] = vec4{b0.x, b0.y, b1.x, b1.y};
