@@ -92,6 +92,15 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Largest of three finite-or-infinite scores in one instruction (the
+// library's maxnum would first quiet each input, which scores never need:
+// they are products of finite values or -inf from a mask).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ vec4 load_stream(const char *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const vec4 *>(p));
 }
@@ -1609,8 +1618,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
             float mxc[NQ];
 #pragma unroll
             for (int c = 0; c < NQ; ++c) {
-                mxc[c] = fmaxf(fmaxf(fmaxf(x[0][c][0], x[0][c][1]), fmaxf(x[0][c][2], x[0][c][3])),
-                               fmaxf(fmaxf(x[1][c][0], x[1][c][1]), fmaxf(x[1][c][2], x[1][c][3])));
+                const float a0 = max3f(x[0][c][0], x[0][c][1], x[0][c][2]);
+                const float a1 = max3f(x[0][c][3], x[1][c][0], x[1][c][1]);
+                mxc[c] = max3f(max3f(a0, a1, x[1][c][2]), x[1][c][3], x[1][c][3]);
                 grow |= mxc[c] > thr[c];
             }
             if (__any(grow)) {
