@@ -55,9 +55,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The decode kernels' source: everything in pa_kernels.hip before its prefill
+# section (element types, decode kernels, merge, launcher).
+DECODE_SECTION_END = b"// ---------------------------------------------------------------- prefill"
+
+
 def kernel_hash() -> str:
+    """Hash of the decode kernels' source, which the committed counter
+    summary was taken with: changes to other kernels in the same file (prefill,
+    cache_write, copies) leave it, and the traffic figure, valid."""
     with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        src = f.read()
+    i = src.find(DECODE_SECTION_END)
+    if i < 0:
+        raise RuntimeError(f"{KERNEL_SRC}: prefill section marker not found")
+    return hashlib.sha256(src[:i]).hexdigest()[:16]
 
 
 def decode_bytes(lens, hq, hkv, d, e, block):
