@@ -1335,6 +1335,7 @@ struct PrefillArgs {
     void *out;
     float qk_scale;  // scale * log2(e)
     int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, max_q, total_rows, tiles;
+    int32_t xcd_heads;  // grid x permuted so a kv head's query heads share an XCD
     int64_t tok_bytes, head_bytes, blk_bytes;
 };
 
@@ -1389,11 +1390,19 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
     const int col = lane & 15;  // key row of the A operand; query column of the scores
     const int kb = lane >> 4;   // k-block of the operands; 4-key group of the scores
     // Grid (heads, sequences, tiles), dispatched x first: the last tiles of
-    // every chunk, which see the most keys, start first.
-    const int h = blockIdx.x;
+    // every chunk, which see the most keys, start first.  Consecutive
+    // workgroups go to the eight XCDs in turn, so with a multiple of eight
+    // heads x = 8 r + x8 runs on XCD x8; when the kv heads are a multiple of
+    // eight too, x maps to query head (8 (r / R) + x8) R + r % R (R query
+    // heads per kv head), which puts all R heads of a kv head on one XCD,
+    // where they read the same keys and values through one L2.
+    const int R = a.Hq / a.Hkv;
+    const int h = a.xcd_heads ? ((((int)blockIdx.x >> 3) / R) * 8 + ((int)blockIdx.x & 7)) * R +
+                                    (((int)blockIdx.x >> 3) % R)
+                              : (int)blockIdx.x;
     const int s = blockIdx.y;
     const int tile = a.tiles - 1 - (int)blockIdx.z;
-    const int g = h / (a.Hq / a.Hkv);
+    const int g = h / R;
 
     // The chunk's rows, clamped so that no access leaves q, out or the table.
     int q0 = a.qstart[s], q1 = a.qstart[s + 1];
@@ -1735,6 +1744,7 @@ static hipError_t launch_prefill_t(const PrefillLaunch &l, hipStream_t st) {
     a.max_q = l.max_q;
     a.total_rows = l.total_rows;
     a.tiles = (l.max_q + kPrefillRows - 1) / kPrefillRows;
+    a.xcd_heads = l.Hkv % 8 == 0 && l.Hq > l.Hkv;
     const int64_t row = (int64_t)l.D * sizeof(T);
     if (l.layout == 0) {
         a.tok_bytes = row * l.Hkv;

@@ -73,6 +73,18 @@ def test_prefill_long_context_chunk():
     assert_fp_close(f64(run(p, "HND"), "f16"), ref(p), "f16")
 
 
+def test_prefill_table_chunks():
+    """Block sizes 1 and 2 with contexts past 1024 blocks: the key loop takes
+    the block table 1024 entries at a time and restarts its pipeline at each
+    such chunk (chunks of 1024 and 2048 keys; the last one ragged)."""
+    print("case B=1", flush=True)
+    p = W.random_prefill(88, "f16", [2500, 1030], [300, 1030], 4, 2, 128, block_size=1)
+    assert_fp_close(f64(run(p, "HND"), "f16"), ref(p), "f16")
+    print("case B=2", flush=True)
+    p = W.random_prefill(89, "bf16", [2100], [129], 4, 4, 64, block_size=2)
+    assert_fp_close(f64(run(p, "NHD"), "bf16"), ref(p), "bf16")
+
+
 def test_prefill_is_causal():
     p = W.random_prefill(84, "bf16", [90], [40], 4, 4, 128, poison=False)
     before = run(p, "NHD")
