@@ -1175,6 +1175,40 @@ def main():
                   "what": "the timed region repeated after the measurement; average launch "
                           "time of each repeat (HIP events on the launch stream)"}
 
+    # The same step on a pool in the other layout (token-major when the
+    # measured one is head-major), timed the same way: reported beside the
+    # line, not part of value.
+    other_layout = None
+    if not args.no_extras:
+        lay2 = "NHD" if args.layout == "HND" else "HND"
+        if lay2 == "HND":
+            kc2 = torch.from_numpy(np.ascontiguousarray(np.swapaxes(p.k_cache, 1, 2))).to(dev)
+            vc2 = torch.from_numpy(np.ascontiguousarray(np.swapaxes(p.v_cache, 1, 2))).to(dev)
+        else:
+            kc2 = torch.from_numpy(p.k_cache).to(dev)
+            vc2 = torch.from_numpy(p.v_cache).to(dev)
+        pools2 = [(kc2, vc2)] + [(kc2.clone(), vc2.clone()) for _ in range(R - 1)]
+
+        def run2(count):
+            for i in range(count):
+                k, v = pools2[i % R]
+                pa.pa_decode_append(q, k_new, v_new, k, v, bt, cl, p.scale, out,
+                                    max_context_len=mcl, partition_size=args.partition,
+                                    workspace=ws, layout=lay2)
+
+        run2(args.warmup)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        run2(args.steps)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        us2 = b0.elapsed_time(b1) * 1e3 / args.steps
+        del pools2, kc2, vc2
+        torch.cuda.empty_cache()
+        other_layout = {"layout": lay2, "kv_layout": "[NB, B, Hkv, D]" if lay2 == "NHD" else "[NB, Hkv, B, D]",
+                        "avg_launch_us": round(us2, 3)}
+        log(f"other layout {lay2}: {us2:.2f} us per launch")
+
     toks = int(lens.sum())
     value = toks * args.steps / wall
     # attention's reads plus the newest rows written into their slots
@@ -1218,6 +1252,13 @@ def main():
         "two_launch_ms_per_step": None if two_launch is None else round(two_launch * 1e3, 5),
         "launch_spread": spread,
     }
+    if other_layout is not None:
+        gbs2 = launch_bytes / (other_layout["avg_launch_us"] * 1e-6) / 1e9
+        other_layout["GB_s"] = round(gbs2, 1)
+        other_layout["frac_of_8000"] = round(gbs2 / HBM_PEAK_GBS, 4)
+        other_layout["what"] = ("the same decode step (same values, same algorithmic bytes) on a pool "
+                                "in the other block layout, one HIP event pair around the launches")
+        result["other_layout"] = other_layout
     if not args.no_extras:
         try:
             ref = stream_reference(launch_bytes)
