@@ -657,6 +657,46 @@ def config_rates(rounds=10, only=None):
         res[label] = r
         del pools, k0, v0
         torch.cuda.empty_cache()
+    # The beams again through pa_decode_shared: each prompt's 32 shared blocks
+    # read once per group of 6 beams (split 512: the prompt is partition 0).
+    label = "beams fp16, shared-prefix decode (16 groups x 6 beams, split 512)"
+    if only is None or label.startswith(only):
+        sc = W.config4(poison=False)
+        p = sc.paged
+        S, Hq, D = p.q.shape
+        gs, gsh = W.config4_groups(sc)
+        k0, v0 = _dev_pool(p.k_cache, "HND"), _dev_pool(p.v_cache, "HND")
+        R = replicas_for(2 * k0.numel() * k0.element_size())
+        pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+        q, bt, cl = _dev(p.q), _dev(p.block_tables), _dev(p.context_lens)
+        gs_d, gsh_d = _dev(gs), _dev(gsh)
+        out = torch.empty_like(q)
+        mcl = int(p.context_lens.max())
+        params = pa.DecodeParams(S, Hq, p.num_kv_heads, D, p.block_size, p.max_blocks_per_seq,
+                                 p.num_blocks, mcl, 512, 1, pa.LAYOUTS["HND"])
+        ws = torch.empty(max(1, pa.pa_decode_shared_workspace_size(params) // 4),
+                         dtype=torch.float32, device="cuda")
+
+        def fs(i):
+            k, v = pools[i % R]
+            pa.pa_decode_shared(q, k, v, bt, cl, gs_d, gsh_d, p.scale, out,
+                                max_shared_blocks=int(gsh.max()), max_context_len=mcl,
+                                partition_size=512, workspace=ws, layout="HND")
+
+        for i in range(2 * R):
+            fs(i)
+        t = time_graph(fs, R, rounds, st)
+        b = decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, W.ELEM_BYTES[p.dtype], p.block_size)
+        u = unique_decode_bytes(p.block_tables, p.context_lens, Hq, p.num_kv_heads, D,
+                                W.ELEM_BYTES[p.dtype], p.block_size)
+        res[label] = {"us": round(t * 1e6, 2),
+                      "kv_tokens_per_s": round(float(p.context_lens.sum()) / t, 1),
+                      "replicas": R, "unique_bytes": u, "GB_s": round(u / t / 1e9, 1),
+                      "frac_of_8000": round(u / t / 8e12, 4), "logical_bytes": b,
+                      "launches": "grouped prefix pass + per-sequence pass + merge",
+                      "bytes": "GB_s and frac_of_8000 on unique bytes (each physical block once)"}
+        del pools, k0, v0
+        torch.cuda.empty_cache()
     return res
 
 
@@ -1042,6 +1082,8 @@ def main():
     ap.add_argument("--gqa", action="store_true",
                     help="time pa_decode on the grouped-query long-context batch only (split 512, "
                          "decode + merge); one JSON line")
+    ap.add_argument("--beams", action="store_true",
+                    help="time pa_decode and pa_decode_shared on the beams batch only; one JSON line")
     ap.add_argument("--block-sweep", action="store_true",
                     help="decode time against block size (1..256), in order / scattered / "
                          "contiguous, on a 16 x 4096-token GQA batch; one JSON line per point")
@@ -1081,6 +1123,9 @@ def main():
         return
     if args.gqa:
         print(json.dumps(config_rates(only="GQA")), flush=True)
+        return
+    if args.beams:
+        print(json.dumps(config_rates(only="beams")), flush=True)
         return
     dev = torch.device("cuda:0")
     t_gen = time.time()

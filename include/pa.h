@@ -195,6 +195,66 @@ int pa_decode_no_alloc(const void *q, const void *k_cache, const void *v_cache,
                        void *out, const pa_decode_params *p, void *stream);
 
 /*
+ * Bytes of workspace pa_decode_shared needs for ``p``: the split-K partials
+ * as in pa_decode_workspace_size (rounded up to 16 bytes), then
+ * 4 * num_seqs bytes (rounded up to 16) for each sequence's count of
+ * partitions the grouped pass computed.  Same checks as
+ * pa_decode_workspace_size; writes the size to *bytes (0 on error).
+ */
+int pa_decode_shared_workspace_size(const pa_decode_params *p, size_t *bytes);
+
+/*
+ * pa_decode for batches whose sequences share leading blocks: parallel
+ * samples of one prompt, beam candidates with common ancestors, requests
+ * with a common system prefix ([Kwon] "Memory Sharing for Complex Decoding
+ * Algorithms": parallel sampling, beam search, shared prefix; [Res] "Sharing
+ * blocks: parallel sampling and copy-on-write").  In the pages the attention
+ * kernel sees only physical block ids and knows nothing of sharing ([Kwon]
+ * "Logical-to-physical separation"), so a shared block is read once per
+ * sequence.  Here the caller, who made the sharing (fork), passes the
+ * groups, and every block in a group's shared prefix is read once per group.
+ *
+ * Groups: group i is sequences group_start[i] .. group_start[i+1] - 1, and
+ * they name the same physical blocks in their first group_shared[i] table
+ * entries (group_start [num_groups + 1] and group_shared [num_groups],
+ * int32 device arrays, 4-byte aligned).  The groups must cover the batch in
+ * order: group_start[0] == 0, non-decreasing, group_start[num_groups] ==
+ * num_seqs (single-sequence groups are fine).  max_shared_blocks (host) is
+ * at least every group_shared[i] and at most max_blocks_per_seq; it sizes
+ * the first launch's grid.
+ *
+ * Work: with split-K partitions of p->partition_size tokens (required > 0),
+ * the partitions that lie wholly inside a group's shared prefix are computed
+ * once per (group, kv head) by a first launch, the group's query heads
+ * (members x query heads per kv head, at most 16) as the score columns of
+ * one matrix-core tile, each column masked at its own member's context
+ * length; it also records, per sequence, how many leading partitions it
+ * computed (in the workspace).  A second launch computes every sequence's
+ * other partitions as pa_decode does, and the merge combines them.  A group
+ * of one sequence, or with more than 16 query heads in all, or whose shared
+ * prefix holds no whole partition, is computed as pa_decode would.
+ *
+ * The result equals pa_decode's within floating-point rounding (the shared
+ * partitions are summed in a different order), and is bitwise deterministic
+ * for fixed inputs, groups and launch configuration.  Every other parameter,
+ * precondition and clamp is pa_decode's; the table entries group members
+ * share are read from the group's first sequence.
+ *
+ * workspace: device pointer (16-byte aligned) to at least
+ * pa_decode_shared_workspace_size(p) bytes; contents on entry do not matter.
+ * Returns PA_ERR_UNSUPPORTED for fp32; PA_ERR_SHAPE for partition_size 0,
+ * num_groups < 0 or > num_seqs, or max_shared_blocks outside [0,
+ * max_blocks_per_seq]; PA_ERR_NULL / PA_ERR_ALIGN for the group arrays when
+ * num_groups > 0; otherwise as pa_decode.  num_groups == 0 computes plain
+ * pa_decode (split-K).  Calls that share a workspace must not overlap.
+ */
+int pa_decode_shared(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens,
+                     const int32_t *group_start, const int32_t *group_shared, int32_t num_groups,
+                     int32_t max_shared_blocks, float scale, void *out,
+                     const pa_decode_params *p, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * decode_append: the decode iteration's write and attention in one launch.
  * For every sequence s with n = context_lens[s] >= 1 the newest token's rows
  * k_new[s], v_new[s] ([num_seqs, num_kv_heads, head_dim], the token at

@@ -8,7 +8,7 @@ is not built, every call raises.
 
 Entry points (same names as the C ABI):
   pa_decode, pa_decode_no_alloc, pa_decode_append, pa_decode_dense, pa_decode_workspace_size,
-  pa_cache_write, pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
+  pa_decode_shared, pa_decode_shared_workspace_size, pa_cache_write, pa_copy_blocks, pa_copy_blocks_layers, pa_swap_blocks, pa_prefill
 and the host block manager (``include/pa_block_manager.h``) as the class
 ``BlockManager`` in ``paged_kv_cache_pa_amd.block_manager``.
 """
@@ -19,7 +19,8 @@ import os
 
 from .build import LIB_PATH
 
-__all__ = ["pa_decode", "pa_decode_no_alloc", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size", "pa_cache_write",
+__all__ = ["pa_decode", "pa_decode_no_alloc", "pa_decode_append", "pa_decode_dense", "pa_decode_workspace_size",
+           "pa_decode_shared", "pa_decode_shared_workspace_size", "pa_cache_write",
            "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers", "pa_swap_blocks",
            "pa_prefill", "PaError",
            "lib",
@@ -101,6 +102,8 @@ def lib():
         L.pa_decode_workspace_size.argtypes = [DP, ctypes.POINTER(SZ)]
         L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
         L.pa_decode_no_alloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, DP, P]
+        L.pa_decode_shared_workspace_size.argtypes = [DP, ctypes.POINTER(SZ)]
+        L.pa_decode_shared.argtypes = [P, P, P, P, P, P, P, I32, I32, ctypes.c_float, P, DP, P, SZ, P]
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, DP, P, SZ, P]
         L.pa_decode_dense.argtypes = [P, P, P, P, ctypes.c_float, P, DP, I32, P, SZ, P]
         L.pa_cache_write.argtypes = [P, P, P, P, P, I32, CP, P]
@@ -111,6 +114,7 @@ def lib():
                                  ctypes.POINTER(PrefillParams), P]
         L.pa_swap_blocks.argtypes = [P, P, I32, P, P, I32, I32, P, I32, CP, P]
         for f in ("pa_decode_workspace_size", "pa_decode", "pa_decode_no_alloc",
+                  "pa_decode_shared_workspace_size", "pa_decode_shared",
                   "pa_decode_append", "pa_decode_dense",
                   "pa_cache_write",
                   "pa_copy_blocks", "pa_copy_blocks_layers", "pa_cache_write_layers",
@@ -239,6 +243,56 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, *,
     _check(lib().pa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                            _ptr(context_lens), float(scale), _ptr(out), ctypes.byref(p),
                            _ptr(ws), nbytes, _stream(stream)), "pa_decode")
+    return out
+
+
+def pa_decode_shared_workspace_size(params: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().pa_decode_shared_workspace_size(ctypes.byref(params), ctypes.byref(n)),
+           "pa_decode_shared_workspace_size")
+    return int(n.value)
+
+
+def pa_decode_shared(q, k_cache, v_cache, block_tables, context_lens, group_start, group_shared,
+                     scale, out, *, max_shared_blocks=None, max_context_len=None,
+                     partition_size=512, workspace=None, stream=None, layout="NHD"):
+    """pa_decode for batches whose sequences share leading blocks (parallel
+    samples, beams, a common prefix): group i is sequences group_start[i] ..
+    group_start[i+1] - 1 (int32 [G + 1], covering the batch in order), whose
+    first group_shared[i] table entries (int32 [G]) name the same blocks.
+    Blocks in a group's shared prefix are read once per group.
+    ``max_shared_blocks`` (host bound on group_shared, default MBS) sizes the
+    grouped grid; ``partition_size`` (> 0) is the split-K partition, and only
+    whole partitions inside a shared prefix are shared.  16-bit types."""
+    import torch
+
+    _need(q, "q", 3)
+    _need(k_cache, "k_cache", 4, q.dtype)
+    _need(v_cache, "v_cache", 4, q.dtype)
+    _need(block_tables, "block_tables", 2, torch.int32)
+    _need(context_lens, "context_lens", 1, torch.int32)
+    _need(group_start, "group_start", 1, torch.int32)
+    _need(group_shared, "group_shared", 1, torch.int32)
+    _need(out, "out", 3, q.dtype)
+    if v_cache.shape != k_cache.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch between k_cache/v_cache or q/out")
+    if block_tables.shape[0] != q.shape[0] or context_lens.shape[0] != q.shape[0]:
+        raise ValueError("block_tables / context_lens must have one row per sequence")
+    n_groups = group_shared.shape[0]
+    if group_start.shape[0] != n_groups + 1:
+        raise ValueError("group_start must have one entry more than group_shared")
+    p = _params_paged(q, k_cache, block_tables, max_context_len, partition_size, layout)
+    if max_shared_blocks is None:
+        max_shared_blocks = p.max_blocks_per_seq
+    need = pa_decode_shared_workspace_size(p)
+    if workspace is None:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().pa_decode_shared(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                  _ptr(context_lens), _ptr(group_start), _ptr(group_shared),
+                                  int(n_groups), int(max_shared_blocks), float(scale), _ptr(out),
+                                  ctypes.byref(p), _ptr(workspace), nbytes, _stream(stream)),
+           "pa_decode_shared")
     return out
 
 

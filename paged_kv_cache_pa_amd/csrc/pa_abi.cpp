@@ -94,6 +94,19 @@ size_t workspace_bytes(const pa_decode_params *p) {
     return (size_t)p->num_seqs * p->num_q_heads * P * (p->head_dim + 2) * sizeof(float);
 }
 
+// Shared-prefix decode: the partials as above, then the per-sequence count
+// of leading partitions the grouped launch computed (int32 [S]), 16-byte
+// aligned.
+size_t skip_offset(const pa_decode_params *p) { return (workspace_bytes(p) + 15) & ~(size_t)15; }
+size_t shared_workspace_bytes(const pa_decode_params *p) {
+    return skip_offset(p) + (((size_t)p->num_seqs * 4 + 15) & ~(size_t)15);
+}
+
+struct Groups {
+    const int32_t *start, *shared;
+    int32_t n, max_shared;
+};
+
 // Pointer checks of a decode call with at least one sequence.
 int check_decode_ptrs(const void *q, const void *k, const void *v, const int32_t *tables,
                       const int32_t *lens, const void *out, bool dense) {
@@ -106,11 +119,12 @@ int check_decode_ptrs(const void *q, const void *k, const void *v, const int32_t
 int run_decode(const void *q, const void *k, const void *v, const int32_t *tables,
                const int32_t *lens, float scale, void *out, const pa_decode_params *p,
                void *ws, size_t ws_bytes, void *stream, bool dense, int32_t max_seq_len,
-               const void *k_new = nullptr, const void *v_new = nullptr) {
+               const void *k_new = nullptr, const void *v_new = nullptr,
+               const Groups *grp = nullptr) {
     if (p->num_seqs == 0) return PA_OK;
     const int pst = check_decode_ptrs(q, k, v, tables, lens, out, dense);
     if (pst != PA_OK) return pst;
-    const size_t need = workspace_bytes(p);
+    const size_t need = grp ? shared_workspace_bytes(p) : workspace_bytes(p);
     if (need) {
         if (!ws || ws_bytes < need) return PA_ERR_WORKSPACE;
         if (!aligned16(ws)) return PA_ERR_ALIGN;
@@ -143,6 +157,14 @@ int run_decode(const void *q, const void *k, const void *v, const int32_t *table
         l.v_new = v_new;
         l.k_w = const_cast<void *>(k);
         l.v_w = const_cast<void *>(v);
+    }
+    if (grp && grp->n > 0) {
+        l.group_start = grp->start;
+        l.group_shared = grp->shared;
+        l.n_groups = grp->n;
+        l.max_shared_blocks = grp->max_shared;
+        l.PSg = p->partition_size;
+        l.skip = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + skip_offset(p));
     }
     const int e = pa::launch_decode(l, stream);
     return hip_status(e);
@@ -222,6 +244,41 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
     if (st != PA_OK) return st;
     return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
                       ws_bytes, stream, false, 0);
+}
+
+int pa_decode_shared_workspace_size(const pa_decode_params *p, size_t *bytes) {
+    if (!bytes || !p) return PA_ERR_NULL;
+    *bytes = 0;
+    const int st = check_decode_shape(p, INT32_MAX, 1);
+    if (st != PA_OK) return st;
+    *bytes = shared_workspace_bytes(p);
+    return PA_OK;
+}
+
+int pa_decode_shared(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, const int32_t *context_lens,
+                     const int32_t *group_start, const int32_t *group_shared, int32_t num_groups,
+                     int32_t max_shared_blocks, float scale, void *out,
+                     const pa_decode_params *p, void *workspace, size_t ws_bytes, void *stream) {
+    const int st = check_paged_shape(p);
+    if (st != PA_OK) return st;
+    if (p->dtype != PA_F16 && p->dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (p->partition_size < 1) return PA_ERR_SHAPE;
+    if (num_groups < 0 || num_groups > p->num_seqs) return PA_ERR_SHAPE;
+    if (max_shared_blocks < 0 || max_shared_blocks > p->max_blocks_per_seq) return PA_ERR_SHAPE;
+    if (p->num_seqs == 0) return PA_OK;
+    if (num_groups > 0) {
+        if (!group_start || !group_shared) return PA_ERR_NULL;
+        if (((uintptr_t)group_start & 3u) || ((uintptr_t)group_shared & 3u)) return PA_ERR_ALIGN;
+        // grouped grid: (group, kv head, shared partition) workgroups of up to 512 threads
+        const int64_t sp = (int64_t)max_shared_blocks * p->block_size / p->partition_size;
+        const int64_t pg = sp < 1 ? 1 : (sp > num_partitions(p) ? num_partitions(p) : sp);
+        if ((int64_t)num_groups * p->num_kv_heads * pg * 512 > 0xFFFFFFFFll)
+            return PA_ERR_UNSUPPORTED;
+    }
+    const Groups g{group_start, group_shared, num_groups, max_shared_blocks};
+    return run_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, p, workspace,
+                      ws_bytes, stream, false, 0, nullptr, nullptr, &g);
 }
 
 static_assert(PA_NO_ALLOC_SCRATCH_BYTES == pa::kNoAllocScratchBytes,

@@ -208,6 +208,16 @@ struct DecodeArgs {
     char *k_w;
     char *v_w;
     int32_t S, Hq, Hkv, NB, MBS, log2B, max_ctx, PS, P;
+    // Shared prefixes: skip[s] leading partitions of sequence s are computed
+    // by the grouped launch (null: none).  The grouped launch itself reads
+    // groups [group_start[i], group_start[i+1]) sharing group_shared[i]
+    // leading table entries, Gh query heads per kv head, Pg partitions per
+    // group in its grid, and writes skip[] for every member.
+    const int32_t *skip;
+    const int32_t *group_start;
+    const int32_t *group_shared;
+    int32_t *skip_out;
+    int32_t Gh, Pg;
     int32_t rank;       // 1: longest-first sequence order (S <= kRankMaxSeqs)
     int32_t spec_blocks;  // table entries a partition can need (fetched before its length)
     int64_t tok_bytes;  // bytes between consecutive tokens of one head
@@ -370,6 +380,40 @@ __device__ void finish_workgroup(const DecodeArgs &a, const float *red, int nw, 
     }
 }
 
+// End of a grouped (shared-prefix) workgroup: red[w][c] for score column c =
+// member c / Gh, head c % Gh; lim[c] is that member's length.  A member whose
+// context ends inside the first partition gets its output row, others the
+// partition's partial; partitions past a member's end are not its own.
+template <typename T, int D>
+__device__ void finish_group(const DecodeArgs &a, const float *red, int nw, int ncol, int s0,
+                             int h, int part, int cols, const int32_t *lim, int tid, int nthr) {
+    for (int i = tid; i < cols * D; i += nthr) {
+        const int c = i / D, d = i % D;
+        const int np = (lim[c] + a.PS - 1) / a.PS;
+        if (part >= np) continue;
+        float M = kNegBig;
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, red[(w * ncol + c) * (D + 2) + D]);
+        float L = 0.0f, A = 0.0f;
+        for (int w = 0; w < nw; ++w) {
+            const float *r = red + (w * ncol + c) * (D + 2);
+            const float cw = fexp2(r[D] - M);
+            L = fmaf(r[D + 1], cw, L);
+            A = fmaf(r[d], cw, A);
+        }
+        const int64_t qh = (int64_t)(s0 + c / a.Gh) * a.Hq + (int64_t)h * a.Gh + c % a.Gh;
+        if (np <= 1) {
+            Elem<T>::store(a.out, qh * D + d, A / L);
+        } else {
+            const int64_t pi = qh * a.P + part;
+            a.ws_acc[pi * D + d] = A;
+            if (d == 0) {
+                a.ws_ml[pi * 2] = M;
+                a.ws_ml[pi * 2 + 1] = L;
+            }
+        }
+    }
+}
+
 // fp32 rows need twice the registers per token, so fp32 workgroups keep 4 waves.
 template <typename T>
 constexpr int max_waves() { return sizeof(T) == 4 ? 4 : kMaxWaves; }
@@ -402,10 +446,16 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     int item, part;
     grid_pos(a, item, part);
     const int h = item % a.Hkv;
+    // Leading partitions of a shared prefix are the grouped launch's (its
+    // count is requested first, so a workgroup with nothing to do leaves
+    // after one round trip; no ranking with a shared prefix, so the
+    // sequence is item / Hkv).
+    const int skip_s = a.skip ? a.skip[item / a.Hkv] : 0;
 
     int s, n;
     bool staged;
     pick_work<MODE>(a, s_len, &s_pick, s_tab, item, part, tid, nthr, s, n, staged);
+    if (part < skip_s) return;
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;  // first query head of the group
@@ -754,7 +804,7 @@ __device__ __forceinline__ int row_swz(int r) {
     else return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
 }
 
-template <typename T, int D, int G, int MODE>
+template <typename T, int D, int G, int MODE, bool GROUPED = false>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a) {
     using E = Elem<T>;
     using M = Mma<T>;
@@ -784,27 +834,76 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     const int tok = lane & 15;   // token of the step this lane loads; head of its score column
     const int kb = lane >> 4;    // k-block: 8 dims of each 32-dim slice; 4 tokens of the score tile
     int item, part;
-    grid_pos(a, item, part);
+    if constexpr (GROUPED) {  // grid (group, kv head) items x Pg partitions
+        part = (int)blockIdx.x % a.Pg;
+        item = (int)blockIdx.x / a.Pg;
+    } else {
+        grid_pos(a, item, part);
+    }
     const int h = item % a.Hkv;
     char *ktile = smem + TAB_BYTES + wave * 2 * TILE;
     char *vtile = ktile + TILE;
 
     int s, n;
     bool staged;
-    pick_work<MODE>(a, s_len, &s_pick, s_tab, item, part, tid, nthr, s, n, staged);
+    int64_t qrow_tok;    // q / out row of score column tok
+    int cols = G;        // score columns in use
+    int lim = INT32_MAX; // grouped: keys at or past it are hidden from column tok
+    if constexpr (GROUPED) {
+        // Shared prefix ([Kwon] "Memory Sharing for Complex Decoding
+        // Algorithms"; [Res] "Sharing blocks: parallel sampling and
+        // copy-on-write"): the members of a group name the same physical
+        // blocks in their first shared table entries, so a partition inside
+        // that prefix is read once, with the members' query heads as the
+        // score columns (member tok / Gh, head tok % Gh), each column masked
+        // at its own member's length.  The first member's table row
+        // addresses the blocks.
+        const int gi = item / a.Hkv;
+        const int s0 = min(max(a.group_start[gi], 0), a.S);
+        const int s1 = min(max(a.group_start[gi + 1], s0), a.S);
+        const int members = s1 - s0;
+        cols = members * a.Gh;
+        const int shared = min(max(a.group_shared[gi], 0), a.MBS);
+        // whole partitions inside the prefix, at most the grid's Pg
+        const int sp = members >= 2 && cols <= G
+                           ? (int)min((int64_t)shared * (1 << a.log2B) / a.PS, (int64_t)a.Pg)
+                           : 0;
+        // every member's count of partitions computed here, for the launch
+        // that computes the rest (an empty member is left to it entirely)
+        if (h == 0 && part == 0)
+            for (int i = tid; i < members; i += nthr)
+                a.skip_out[s0 + i] = clamp_len(a.lens[s0 + i], a.max_ctx) > 0 ? sp : 0;
+        if (part >= sp) return;
+        const int mi = tok / a.Gh;
+        lim = tok < cols ? clamp_len(a.lens[s0 + mi], a.max_ctx) : 0;
+        qrow_tok = (int64_t)(s0 + mi) * a.Hq + (int64_t)h * a.Gh + tok % a.Gh;
+        int nmax = lim;  // the longest member bounds the keys read
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off, 64));
+        n = __builtin_amdgcn_readfirstlane(nmax);
+        s = s0;
+        staged = false;
+        if (tid < 16) s_len[tid] = lim;  // for the epilogue
+    } else {
+        // (as in decode_kernel: the shared-prefix count first)
+        const int skip_s = a.skip ? a.skip[item / a.Hkv] : 0;
+        pick_work<MODE>(a, s_len, &s_pick, s_tab, item, part, tid, nthr, s, n, staged);
+        if (part < skip_s) return;
+        qrow_tok = (int64_t)s * a.Hq + (int64_t)h * G + tok;
+    }
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;
 
-    // B operand of S^T = K Q^T: head tok (zero for tok >= G), dims 32 i + 8 kb ...
+    // B operand of S^T = K Q^T: column tok (zero for tok >= cols), dims 32 i + 8 kb ...
     vec4 qb[KL];
 #pragma unroll
     for (int i = 0; i < KL; ++i)
-        qb[i] = tok < G ? load_cached(a.q + ((qrow0 + tok) * D + 32 * i + 8 * kb) * 2)
-                        : vec4{0u, 0u, 0u, 0u};
+        qb[i] = tok < cols ? load_cached(a.q + (qrow_tok * D + 32 * i + 8 * kb) * 2)
+                           : vec4{0u, 0u, 0u, 0u};
 
     if (tb >= te) {
-        if (part == 0)
+        if (!GROUPED && part == 0)
             for (int i = tid; i < G * D; i += nthr) E::store(a.out, qrow0 * D + i, 0.0f);
         return;
     }
@@ -914,6 +1013,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
             for (int jj = 0; jj < 4; ++jj) {
                 x[jj] = sc[jj] * a.qk_scale;
                 if (MASKED && ctb + j * kStepTokens + 4 * kb + jj >= cte) x[jj] = -__builtin_inff();
+                if (GROUPED && ctb + j * kStepTokens + 4 * kb + jj >= lim) x[jj] = -__builtin_inff();
             }
             // lazy running max: the rescale is a rare wave-uniform branch
             float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -995,7 +1095,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
         }
     }
     __syncthreads();
-    finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
+    if constexpr (GROUPED)
+        finish_group<T, D>(a, red, nw, G, s, h, part, cols, s_len, tid, nthr);
+    else
+        finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
 }
 
 // Combines the partitions of one (sequence, query head): with M the largest
@@ -1117,6 +1220,60 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(
     }
 }
 
+// The same combination for up to kMergeRowsP partitions, several rows per
+// workgroup: thread t takes chunk t % (D/4) of row t / (D/4) and all its
+// partitions (requested together with the length, addresses clamped to the
+// P allocated partitions), summed in partition order; no LDS, no barrier.
+constexpr int kMergeRowsP = 8;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(
+    const float *ws_acc, const float *ws_ml, const int32_t *lens, void *out, int32_t rows,
+    int32_t Hq, int32_t P, int32_t PS, int32_t max_ctx) {
+    constexpr int C4 = D / 4;
+    constexpr int RPW = kMergeThreads / C4;  // rows per workgroup
+    const int t = threadIdx.x;
+    const int64_t qh = (int64_t)blockIdx.x * RPW + t / C4;
+    if (qh >= rows) return;
+    const int c = t % C4;
+    const int s = (int)(qh / Hq);
+    const float *ml = ws_ml + qh * P * 2;
+    const float4 *ac = reinterpret_cast<const float4 *>(ws_acc + qh * P * D);
+    float mp[kMergeRowsP], lp[kMergeRowsP];
+    float4 x[kMergeRowsP];
+#pragma unroll
+    for (int k = 0; k < kMergeRowsP; ++k) {
+        const int pc = k < P ? k : P - 1;
+        mp[k] = ml[2 * pc];
+        lp[k] = ml[2 * pc + 1];
+        x[k] = ac[(int64_t)pc * C4 + c];
+    }
+    const int n = clamp_len(lens[s], max_ctx);
+    const int np = (n + PS - 1) / PS;
+    if (np <= 1) return;  // written by the decode kernel
+    float M = kNegBig;
+#pragma unroll
+    for (int k = 0; k < kMergeRowsP; ++k) M = k < np ? fmaxf(M, mp[k]) : M;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMergeRowsP; ++k) {
+        if (k < np) {
+            const float w = fexp2(mp[k] - M);
+            a.x = fmaf(x[k].x, w, a.x);
+            a.y = fmaf(x[k].y, w, a.y);
+            a.z = fmaf(x[k].z, w, a.z);
+            a.w = fmaf(x[k].w, w, a.w);
+            L = fmaf(lp[k], w, L);
+        }
+    }
+    const int64_t o = qh * D + 4 * c;
+    Elem<T>::store(out, o + 0, a.x / L);
+    Elem<T>::store(out, o + 1, a.y / L);
+    Elem<T>::store(out, o + 2, a.z / L);
+    Elem<T>::store(out, o + 3, a.w / L);
+}
+
 // Workgroups of one kernel that a CU holds at once, at a given block size and
 // dynamic LDS, times the CU count of the current device.  Queried once per
 // (kernel, waves, device) and cached; the query itself is host-only.
@@ -1193,6 +1350,11 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.max_ctx = l.max_ctx;
     a.PS = l.PS;
     a.P = l.P;
+    a.skip = nullptr;
+    a.group_start = a.group_shared = nullptr;
+    a.skip_out = nullptr;
+    a.Gh = l.Hq / l.Hkv;
+    a.Pg = 1;
     // Ranking costs the workgroup one dependent round trip; it pays only when
     // the grid is too large to be resident at once, so that order matters.
     a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512) ? 1 : 0;
@@ -1242,12 +1404,51 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
         lds = lds_of(nw);
     }
     (void)hipGetLastError();  // an error left by other code is not this launch's
+    if (l.n_groups > 0) {
+        // The shared prefixes first: one workgroup per (group, kv head,
+        // shared partition), the group's query heads as up to 16 score
+        // columns; it also writes skip[] for the launch below.
+        if constexpr (sizeof(T) == 2) {
+            DecodeArgs g = a;
+            g.PS = l.PSg;
+            g.rank = 0;
+            g.group_start = l.group_start;
+            g.group_shared = l.group_shared;
+            g.skip_out = l.skip;
+            const int64_t sp_max = (int64_t)l.max_shared_blocks * B / l.PSg;
+            g.Pg = (int32_t)(sp_max < 1 ? 1 : (sp_max > l.P ? l.P : sp_max));
+            const int64_t gwgs = (int64_t)l.n_groups * l.Hkv * g.Pg;
+            using Kern = void (*)(DecodeArgs);
+            const Kern gfn = l.B >= kStepTokens ? decode_mma_kernel<T, D, 16, kPagedWide, true>
+                                                : decode_mma_kernel<T, D, 16, kPagedNarrow, true>;
+            auto glds = [&](int w) {
+                return max2((size_t)kTableChunk * 4 + (size_t)w * 2 * kStepTokens * 2 * D,
+                            (size_t)w * 16 * (D + 2) * 4);
+            };
+            const void *gref = (const void *)decode_mma_kernel<T, D, 16, kPagedWide, true>;
+            const int gnw = pick_waves(gref, gref, gwgs, glds(8), glds(4));
+            hipLaunchKernelGGL(gfn, dim3((unsigned)gwgs), dim3(64 * gnw), glds(gnw), st, g);
+            const hipError_t ge = hipGetLastError();
+            if (ge != hipSuccess) return ge;
+            a.skip = l.skip;
+            a.rank = 0;
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     hipLaunchKernelGGL(fn, grid, dim3(64 * nw), lds, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || l.PS == 0) return e;
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)l.S * l.Hq)),
-                       dim3(kMergeThreads), 0, st,
-                       a.ws_acc, a.ws_ml, l.lens, l.out, l.Hq, l.P, l.PS, l.max_ctx);
+    const int64_t rows = (int64_t)l.S * l.Hq;
+    if (l.P <= kMergeRowsP) {
+        constexpr int RPW = kMergeThreads / (D / 4);
+        hipLaunchKernelGGL((merge_rows_kernel<T, D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
+                           dim3(kMergeThreads), 0, st, a.ws_acc, a.ws_ml, l.lens, l.out,
+                           (int32_t)rows, l.Hq, l.P, l.PS, l.max_ctx);
+    } else {
+        hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st,
+                           a.ws_acc, a.ws_ml, l.lens, l.out, l.Hq, l.P, l.PS, l.max_ctx);
+    }
     return hipGetLastError();
 }
 

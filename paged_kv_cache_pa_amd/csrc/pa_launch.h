@@ -27,6 +27,16 @@ struct DecodeLaunch {
     // position n - 1 of each sequence through k_w / v_w while attending.
     const void *k_new = nullptr, *v_new = nullptr;
     void *k_w = nullptr, *v_w = nullptr;
+    // Shared prefixes (paged, 16-bit, n_groups > 0): a grouped launch first
+    // computes, once per group, the leading partitions (of size PSg tokens)
+    // its members share and writes each member's count of them to skip[S];
+    // the usual launch then computes the rest.
+    const int32_t *group_start = nullptr;   // [n_groups + 1], device
+    const int32_t *group_shared = nullptr;  // [n_groups], device
+    int32_t *skip = nullptr;                // [S], device (in the workspace)
+    int32_t n_groups = 0;
+    int32_t max_shared_blocks = 0;          // bound on group_shared (host)
+    int32_t PSg = 0;
 };
 
 // Returns 0 on success, else the hipError_t of the failed launch.

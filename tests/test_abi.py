@@ -386,3 +386,38 @@ def test_grid_thread_count_fits_32_bits(L):
     p = params(num_seqs=65535, num_q_heads=128, num_kv_heads=128, head_dim=128,
                max_blocks_per_seq=1, block_size=16, max_context_len=16, num_blocks=64)
     assert L.pa_decode_workspace_size(ctypes.byref(p), ctypes.byref(ctypes.c_size_t())) == OK
+
+
+def test_decode_shared_checks(L):
+    """pa_decode_shared validates its extra arguments (16-bit types only, a
+    split, a group count within the batch, a shared-block bound within the
+    table row, the group arrays) before any HIP call, and its workspace is
+    pa_decode's rounded up to 16 bytes plus one int32 per sequence."""
+    b = Buf()
+
+    def call(p, gs=b.p, gsh=b.p, ng=2, msb=4, ws=None, nbytes=0):
+        return L.pa_decode_shared(b.p, b.p, b.p, b.p, b.p, gs, gsh, ng, msb,
+                                  ctypes.c_float(0.125), b.p,
+                                  None if p is None else ctypes.byref(p), ws, nbytes, None)
+
+    half = dict(dtype=1, partition_size=32)
+    assert call(None) == NULL
+    assert call(params(dtype=0, partition_size=32)) == UNSUP      # fp32: no matrix-core tile
+    assert call(params(dtype=1)) == SHAPE                         # no split
+    assert call(params(**half), ng=-1) == SHAPE
+    assert call(params(**half), ng=5) == SHAPE                    # more groups than sequences
+    assert call(params(**half), msb=-1) == SHAPE
+    assert call(params(**half), msb=8) == SHAPE                   # past max_blocks_per_seq (7)
+    assert call(params(num_seqs=0, **half), ng=0) == OK           # nothing to do
+    assert call(params(**half), gs=None) == NULL
+    assert call(params(**half), gsh=None) == NULL
+    assert call(params(**half), gs=b.odd) == ALIGN
+    assert call(params(**half), gsh=b.odd) == ALIGN
+    # the workspace: 4 x 8 x ceil(112 / 32) x 66 x 4 bytes of partials, then 4 x 4
+    p = params(**half)
+    assert pa.pa_decode_shared_workspace_size(p) == 4 * 8 * 4 * 66 * 4 + 16
+    assert call(p, ws=b.p, nbytes=4 * 8 * 4 * 66 * 4) == WS       # room for the partials only
+    # max_context_len within one partition: no partials, the per-sequence counts only
+    p1 = params(dtype=1, partition_size=128)
+    assert pa.pa_decode_shared_workspace_size(p1) == 16
+    assert call(p1, ws=None, nbytes=0) == WS

@@ -347,6 +347,59 @@ def config4(seed=404, poison=True, groups=16, beams=6, prompt_len=512, NB=2048) 
                         stem_block, NB - len(free))
 
 
+def random_shared(seed, dtype, groups, hq, hkv, d, block_size=16, extra_blocks=3):
+    """Seeded decode batch whose sequences come in groups that share leading
+    blocks (parallel samples or beams after a fork): ``groups`` =
+    [(shared_blocks, [member context lengths]), ...] in batch order.  The
+    members of a group name the same physical blocks in their first
+    shared_blocks table entries, then blocks of their own; every block sits
+    at a seeded place in the pool.  Shared blocks are filled whole (they hold
+    a prefix every member has computed); a member's own blocks only up to
+    its length, the rest of the pool is NaN.  Returns (Paged, group_start
+    [G + 1], group_shared [G]) as int32 arrays."""
+    rng = np.random.default_rng(seed)
+    B = block_size
+    lens = [int(n) for _, ms in groups for n in ms]
+    S = len(lens)
+    mbs = max(1, max(max(sb, max((int(n) + B - 1) // B for n in ms)) for sb, ms in groups))
+    need = sum(sb + sum(max(0, (int(n) + B - 1) // B - sb) for n in ms) for sb, ms in groups)
+    NB = need + extra_blocks
+    ids = iter(rng.permutation(NB).astype(np.int32))
+    table = np.full((S, mbs), -1, dtype=np.int32)
+    k = nan_fill((NB, B, hkv, d), dtype)
+    v = nan_fill((NB, B, hkv, d), dtype)
+    starts, shared = [0], []
+    s = 0
+    for sb, ms in groups:
+        common = [int(next(ids)) for _ in range(sb)]
+        for b in common:
+            k[b] = randn(rng, (B, hkv, d), dtype)
+            v[b] = randn(rng, (B, hkv, d), dtype)
+        for n in ms:
+            table[s, :sb] = common
+            for j in range(sb, (int(n) + B - 1) // B):
+                b = int(next(ids))
+                table[s, j] = b
+                fill = min(B, int(n) - j * B)
+                k[b, :fill] = randn(rng, (fill, hkv, d), dtype)
+                v[b, :fill] = randn(rng, (fill, hkv, d), dtype)
+            s += 1
+        starts.append(s)
+        shared.append(sb)
+    q = randn(rng, (S, hq, d), dtype)
+    p = Paged(dtype, q, k, v, table, np.array(lens, dtype=np.int32), 1.0 / math.sqrt(d), B, 0,
+              name=f"shared-{dtype}-s{seed}")
+    return p, np.array(starts, dtype=np.int32), np.array(shared, dtype=np.int32)
+
+
+def config4_groups(sc: "BeamScenario"):
+    """Config 4's sharing as groups: each prompt's beams, sharing its 512-token
+    prompt (32 blocks; the partly filled stem block is copied on write)."""
+    starts = np.arange(0, (sc.groups + 1) * sc.beams, sc.beams, dtype=np.int32)
+    shared = np.full(sc.groups, sc.prompt_len // sc.paged.block_size, dtype=np.int32)
+    return starts, shared
+
+
 CONFIG5_LENS = (4096, 10000, 12000, 16384)
 
 
