@@ -658,8 +658,9 @@ def config_rates(rounds=10, only=None):
         del pools, k0, v0
         torch.cuda.empty_cache()
     # The beams again through pa_decode_shared: each prompt's 32 shared blocks
-    # read once per group of 6 beams (split 512: the prompt is partition 0).
-    label = "beams fp16, shared-prefix decode (16 groups x 6 beams, split 512)"
+    # read once per group of 6 beams (split 256: the prompt is partitions 0
+    # and 1), and pa_decode with the same split for comparison.
+    label = "beams fp16, shared-prefix decode (16 groups x 6 beams, split 256)"
     if only is None or label.startswith(only):
         sc = W.config4(poison=False)
         p = sc.paged
@@ -672,8 +673,9 @@ def config_rates(rounds=10, only=None):
         gs_d, gsh_d = _dev(gs), _dev(gsh)
         out = torch.empty_like(q)
         mcl = int(p.context_lens.max())
+        ps = 256
         params = pa.DecodeParams(S, Hq, p.num_kv_heads, D, p.block_size, p.max_blocks_per_seq,
-                                 p.num_blocks, mcl, 512, 1, pa.LAYOUTS["HND"])
+                                 p.num_blocks, mcl, ps, 1, pa.LAYOUTS["HND"])
         ws = torch.empty(max(1, pa.pa_decode_shared_workspace_size(params) // 4),
                          dtype=torch.float32, device="cuda")
 
@@ -681,11 +683,18 @@ def config_rates(rounds=10, only=None):
             k, v = pools[i % R]
             pa.pa_decode_shared(q, k, v, bt, cl, gs_d, gsh_d, p.scale, out,
                                 max_shared_blocks=int(gsh.max()), max_context_len=mcl,
-                                partition_size=512, workspace=ws, layout="HND")
+                                partition_size=ps, workspace=ws, layout="HND")
+
+        def fp(i):
+            k, v = pools[i % R]
+            pa.pa_decode(q, k, v, bt, cl, p.scale, out, max_context_len=mcl, partition_size=ps,
+                         workspace=ws, layout="HND")
 
         for i in range(2 * R):
             fs(i)
+            fp(i)
         t = time_graph(fs, R, rounds, st)
+        t_plain = time_graph(fp, R, rounds, st)
         b = decode_bytes(p.context_lens, Hq, p.num_kv_heads, D, W.ELEM_BYTES[p.dtype], p.block_size)
         u = unique_decode_bytes(p.block_tables, p.context_lens, Hq, p.num_kv_heads, D,
                                 W.ELEM_BYTES[p.dtype], p.block_size)
@@ -693,6 +702,7 @@ def config_rates(rounds=10, only=None):
                       "kv_tokens_per_s": round(float(p.context_lens.sum()) / t, 1),
                       "replicas": R, "unique_bytes": u, "GB_s": round(u / t / 1e9, 1),
                       "frac_of_8000": round(u / t / 8e12, 4), "logical_bytes": b,
+                      "pa_decode_same_split_us": round(t_plain * 1e6, 2),
                       "launches": "grouped prefix pass + per-sequence pass + merge",
                       "bytes": "GB_s and frac_of_8000 on unique bytes (each physical block once)"}
         del pools, k0, v0

@@ -882,7 +882,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
         for (int off = 1; off < 16; off <<= 1) nmax = max(nmax, __shfl_xor(nmax, off, 64));
         n = __builtin_amdgcn_readfirstlane(nmax);
         s = s0;
-        staged = false;
+        // the partition's table entries, requested with the lengths (they
+        // do not depend on them; the loop's first chunk uses them)
+        if constexpr (MODE != kDense) {
+            const int b0 = (part * a.PS) >> a.log2B;
+            stage_table(a.tables + (int64_t)s0 * a.MBS, b0,
+                        min(min(kTableChunk, a.spec_blocks), a.MBS - b0), a.NB, s_tab, tid, nthr);
+        }
+        staged = true;
         if (tid < 16) s_len[tid] = lim;  // for the epilogue
     } else {
         // (as in decode_kernel: the shared-prefix count first)
@@ -1412,6 +1419,7 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
             DecodeArgs g = a;
             g.PS = l.PSg;
             g.rank = 0;
+            g.spec_blocks = (int32_t)(((l.PSg < l.max_ctx ? l.PSg : l.max_ctx) + B - 1) / B);
             g.group_start = l.group_start;
             g.group_shared = l.group_shared;
             g.skip_out = l.skip;
