@@ -9,7 +9,11 @@ its copy-on-write and new-token writes) at partition sizes that share 0, 1,
 prefix, empty members, single-sequence groups, a group too wide for one
 16-column tile (computed unshared), grouped-query heads, head dim 64 and
 block size 8 (steps spanning blocks), both pool layouts; a workspace full
-of NaN; repeated calls (same bits); no groups (same bits as pa_decode)."""
+of NaN; repeated calls (same bits); no groups (same bits as pa_decode).
+Each sequence's count of partitions taken by the grouped pass is read back
+from the workspace, and the shared partitions are shown to be read through
+the group's first sequence: with the other members' shared table entries
+pointed at a NaN block the result is unchanged."""
 from __future__ import annotations
 
 import numpy as np
@@ -32,7 +36,27 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-def run_shared(p, gstart, gshared, layout, ps, tensors=None, max_shared=None, skips=None):
+def poisoned_table(p, gs, sp, ps, nan_block):
+    """The table with every member but the first of each group pointed at a
+    NaN block for its shared partitions (sp per sequence): the result stays
+    exact only if those partitions are read once, through the group's first
+    sequence (as pa_decode_shared states)."""
+    t = p.block_tables.copy()
+    for i in range(len(gs) - 1):
+        for s in range(gs[i] + 1, gs[i + 1]):
+            nb = int(sp[s]) * ps // p.block_size
+            if nb > 0:
+                t[s, :nb] = nan_block
+    return t
+
+
+def unused_block(p):
+    used = set(int(b) for b in p.block_tables.ravel() if b >= 0)
+    return next(b for b in range(p.k_cache.shape[0]) if b not in used)
+
+
+def run_shared(p, gstart, gshared, layout, ps, tensors=None, max_shared=None, skips=None,
+               table=None):
     """pa_decode_shared with a NaN-filled workspace; returns the host output
     (and appends to ``skips`` each sequence's count of partitions the
     grouped pass computed, read back from the workspace)."""
@@ -41,6 +65,8 @@ def run_shared(p, gstart, gshared, layout, ps, tensors=None, max_shared=None, sk
     import paged_kv_cache_pa_amd as pa
 
     q, k, v, bt, cl = tensors if tensors is not None else upload(p, layout)
+    if table is not None:  # in place of the block table
+        bt = to_dev(table)
     S, Hq, D = p.q.shape
     mcl = int(p.context_lens.max())
     P = -(-mcl // ps) if mcl > ps else 1
@@ -81,8 +107,13 @@ def test_config4_beams(beams, layout):
         skips = []
         got = run_shared(pw, gs, gsh, layout, ps, tensors=t, skips=skips)
         assert_fp_close(f64(got, "f16"), ref, "f16", f"config4 shared {layout} partition {ps}")
-        # every beam's prompt partitions came from its group's pass
+        # every beam's prompt partitions came from its group's pass, read
+        # through the group's first beam
         assert (skips[0] == shared_parts).all(), (ps, skips[0])
+        table = poisoned_table(pw, gs, skips[0], ps, unused_block(pw))
+        got = run_shared(pw, gs, gsh, layout, ps, tensors=t, table=table)
+        assert_fp_close(f64(got, "f16"), ref, "f16", f"config4 shared {layout} partition {ps}, "
+                                                     "the other beams' prompt entries poisoned")
     plain = run_decode(pw, partition_size=512, tensors=t, layout=layout)
     assert_fp_close(f64(run_shared(pw, gs, gsh, layout, 512, tensors=t), "f16"), f64(plain, "f16"),
                     "f16", "shared vs pa_decode")
@@ -120,6 +151,9 @@ def test_synthetic_groups_mha(dtype, d, B, layout):
             sp = sb * B // ps if len(ms) >= 2 else 0
             want += [sp if n > 0 else 0 for n in ms]
         assert (skips[0] == np.array(want)).all(), (ps, skips[0], want)
+        got = run_shared(p, gs, gsh, layout, ps, tensors=t,
+                         table=poisoned_table(p, gs, want, ps, unused_block(p)))
+        assert_fp_close(f64(got, dtype), ref, dtype, f"shared mha {dtype} {layout} ps {ps} poisoned")
         assert (f64(got, dtype)[8] == 0).all(), "the empty member's row is zero"
 
 
@@ -140,6 +174,9 @@ def test_synthetic_groups_gqa(layout):
         sp = 6 * 16 // ps
         want = [sp] * 8 + [0] * 9 + [2 * 16 // ps] * 2 + [0] * 2
         assert (skips[0] == np.array(want)).all(), (ps, skips[0], want)
+        got = run_shared(p, gs, gsh, layout, ps, tensors=t,
+                         table=poisoned_table(p, gs, want, ps, unused_block(p)))
+        assert_fp_close(f64(got, "bf16"), ref, "bf16", f"shared gqa {layout} ps {ps} poisoned")
 
 
 def test_deterministic_and_no_groups():
