@@ -1313,7 +1313,8 @@ static int64_t resident_workgroups(const void *fn, int nw, size_t lds) {
     return r;
 }
 
-// Waves per workgroup.  8 waves halve the steps each wave walks and double
+// Waves per workgroup of the VALU decode kernel (the matrix-core kernel has
+// its own rule at its launch).  8 waves halve the steps each wave walks and double
 // the loads a workgroup keeps in flight, which pays when the grid is small,
 // but only while every workgroup is still resident at once: a grid that
 // spills into a second round of workgroups finishes in two round trips of
@@ -1398,8 +1399,13 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
         // The wave count follows one instantiation for every address mode, so
         // paged and dense launches of one shape split the work identically
         // (and give identical bits).
+        // 8 waves only when the whole grid is resident at 8: past that, 4
+        // waves ran 10-20% faster on the long-context grouped-query batch at
+        // every partition size from 320 to 448 tokens (grids of 600-900
+        // workgroups, a third of them without work), where the VALU
+        // kernel's rule would take 8.
         const void *ref = (const void *)decode_mma_kernel<T, D, G, kPagedWide>;
-        nw = pick_waves(ref, ref, wgs, lds_of(8), lds_of(4));
+        nw = wgs <= resident_workgroups(ref, 8, lds_of(8)) ? 8 : 4;
         lds = lds_of(nw);
     } else {
         auto lds_of = [&](int w) { return max2((size_t)kTableChunk * 4, red_bytes(w)); };
@@ -1434,7 +1440,7 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
                             (size_t)w * 16 * (D + 2) * 4);
             };
             const void *gref = (const void *)decode_mma_kernel<T, D, 16, kPagedWide, true>;
-            const int gnw = pick_waves(gref, gref, gwgs, glds(8), glds(4));
+            const int gnw = gwgs <= resident_workgroups(gref, 8, glds(8)) ? 8 : 4;
             hipLaunchKernelGGL(gfn, dim3((unsigned)gwgs), dim3(64 * gnw), glds(gnw), st, g);
             const hipError_t ge = hipGetLastError();
             if (ge != hipSuccess) return ge;
