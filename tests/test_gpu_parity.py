@@ -132,8 +132,11 @@ def test_config5_gqa_split(layout):
     p = W.config5()
     ref = ref_decode(p)
     t = upload(p, layout)
-    got = run_decode(p, partition_size=512, tensors=t, layout=layout)
-    check(p, got, ref, f"config5 {layout} partition 512")
+    # 512: the configured split (512 workgroups); 384 and 336: grids of 688
+    # and 784 workgroups, more than fit at once, on 4-wave workgroups
+    for ps in (512, 384, 336):
+        got = run_decode(p, partition_size=ps, tensors=t, layout=layout)
+        check(p, got, ref, f"config5 {layout} partition {ps}")
     got0 = run_decode(p, partition_size=0, tensors=t, layout=layout)
     check(p, got0, ref, f"config5 {layout} no split")
 
