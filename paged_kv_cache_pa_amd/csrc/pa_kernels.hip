@@ -1,5 +1,6 @@
-// pa_kernels.hip -- gfx950 (CDNA4) kernels for paged decode attention,
-// cache_write and copy_blocks.
+// pa_kernels.hip -- gfx950 (CDNA4) kernels for paged decode attention (and
+// its split-K merge), prefill over the paged cache, cache_write and block
+// copies.
 //
 // Pages cited (by title, then section / equation / figure):
 //   [Kwon] "Efficient Memory Management for Large Language Model Serving with
@@ -38,11 +39,12 @@
 //    arithmetic.  The reduction order depends only on logical token order,
 //    never on where blocks sit, so paged and dense results are bitwise equal
 //    and invariant to block placement.
-//  * Scheduling: for batches of up to 256 sequences every workgroup ranks the
-//    sequences by context length (longest first, ties by index) and takes
-//    the sequence whose rank matches its grid position, so the longest
-//    sequences start first and the tail of the launch is short.  Which
-//    workgroup computes a row never changes its arithmetic.
+//  * Scheduling: for unsplit launches of up to 256 sequences with more than
+//    512 (sequence, kv head) items (more than the chip holds at once), every
+//    workgroup ranks the sequences by context length (longest first, ties
+//    by index) and takes the sequence whose rank matches its grid position,
+//    so the longest sequences start first and the tail of the launch is
+//    short.  Which workgroup computes a row never changes its arithmetic.
 //  * Split-K: partition p covers tokens [p*PS, (p+1)*PS) and writes its
 //    unnormalised partial (acc, m, l) to the workspace; a merge kernel then
 //    combines the partitions by the log-sum-exp identity ([Int] "The kernel
