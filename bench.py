@@ -181,6 +181,20 @@ def paged_dense_ratio(points, rounds=15, warm=3):
     return res
 
 
+def settle(run_once, seconds):
+    """Repeat run_once() (GPU work, synchronized after each call) for
+    ``seconds`` of wall time before a leg is timed, so that the GPU runs at
+    the clock it holds under sustained load: started cold, prefill read 524 /
+    648 TFLOP/s where the same launches read 587-592 / 729-740 after 0.1 s
+    or more of work."""
+    import torch
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        run_once()
+        torch.cuda.synchronize()
+
+
 def time_group(fn, n, stream):
     """Average seconds per call of n back-to-back calls between one event pair."""
     import torch
@@ -219,8 +233,7 @@ def time_graph(fn, n, rounds, stream, min_calls=16):
         for i in range(m):
             fn(i)
     torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
+    settle(g.replay, 0.05)
     ts = []
     for _ in range(rounds):
         a = torch.cuda.Event(enable_timing=True)
@@ -320,8 +333,7 @@ def stream_reference(nbytes, replicas=4, rounds=10):
             raise RuntimeError(f"{what} failed: hipError {rc}")
 
     def timed(f, moved):
-        for i in range(2 * replicas):
-            f(i)
+        settle(lambda: [f(i) for i in range(4 * replicas)], 0.05)
         t = float(np.median([time_group(f, 4 * replicas, st) for _ in range(rounds)]))
         return round(moved / t / 1e9, 1)
 
@@ -585,8 +597,7 @@ def prefill_rate(rounds=10, d=128):
             pa.pa_prefill(q, k, v, table, cl, qs, 1.0 / np.sqrt(d), out, max_query_len=chunk,
                           max_context_len=ctx, layout="HND")
 
-        for i in range(4 * R):
-            f(i)
+        settle(lambda: [f(i) for i in range(4 * R)], 0.25)
         # 4 R launches back to back per event pair (the replicas cycled), so
         # the events' own cost and the gaps between groups stay small
         t = float(np.median([time_group(f, 4 * R, st) for _ in range(rounds)]))
