@@ -1564,20 +1564,19 @@ static_assert(kPrefillRows == kPrefillTileRows, "the host checks grid z with kPr
 
 // 16 bytes per lane from global memory straight into LDS: lane i's piece
 // lands at LDS byte address lds + 16 i (lds wave-uniform).  M0 carries the
-// LDS address and is restored afterwards.  The load counts in vmcnt like any
-// other vector load; the compiler does not track it, so the caller waits
-// (lds_dma_wait) before any wave reads what it wrote.
+// LDS address; it is an operand of the asm, so the compiler loads it (and
+// knows it is clobbered).  The load counts in vmcnt like any other vector
+// load; the compiler does not track it, so the caller waits (lds_dma_wait)
+// before any wave reads what it wrote.
 __device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
-    uint32_t save;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(save)
-        : "v"(g), "s"(lds)
-        : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+// The same with a wave-uniform 64-bit base in scalar registers and a
+// per-lane 32-bit offset (the instruction adds them), which saves the
+// per-lane 64-bit address.
+__device__ __forceinline__ void lds_dma16_s(const char *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds)
+                 : "memory");
 }
 __device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -1752,8 +1751,8 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                     const int ins = wave * NI + i;
                     const uint32_t dk = lds0 + (uint32_t)((st * 2 + 0) * TILEB + ins * 1024);
                     const uint32_t dv = lds0 + (uint32_t)((st * 2 + 1) * TILEB + ins * 1024);
-                    lds_dma16(a.k + base[i] + lane_off[i], __builtin_amdgcn_readfirstlane(dk));
-                    lds_dma16(a.v + base[i] + lane_off[i], __builtin_amdgcn_readfirstlane(dv));
+                    lds_dma16_s(a.k + base[i], lane_off[i], __builtin_amdgcn_readfirstlane(dk));
+                    lds_dma16_s(a.v + base[i], lane_off[i], __builtin_amdgcn_readfirstlane(dv));
                 }
                 return;
             }
