@@ -1779,9 +1779,34 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
 
         // One pair of 16-key sub-tiles (keys key0 .. key0 + 31, rows 16 u ..
         // 16 u + 31 of stage st).
-        auto pair = [&](int st, int u, int key0) {
+        // K operands (A of S^T = K Q^T) of both 16-key sub-tiles of a pair.
+        // The second pair of a tile gets its operands requested under the
+        // first pair's softmax and P V (knext), so its score products need
+        // not wait for LDS.
+        vec4 knext[2][KL];
+        auto loadK = [&](int st, int u, vec4 (&kk)[2][KL]) __attribute__((always_inline)) {
             const char *kt = &s_kv[st][0][0] + 16 * u * ROWB;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < KL; ++i)
+                    kk[hh][i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
+        };
+        auto pair = [&](int st, int u, int key0, bool kready, bool pre) __attribute__((always_inline)) {
             const char *vt = &s_kv[st][1][0] + 16 * u * ROWB;
+            const bool masked = key0 + 31 > mask_free;  // wave-uniform
+            // K operands of both sub-tiles, requested together (the second
+            // sub-tile's rows are in LDS whether or not they are used), or
+            // taken from the previous pair's request
+            vec4 ka2[2][KL];
+            if (kready) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int i = 0; i < KL; ++i) ka2[hh][i] = knext[hh][i];
+            } else {
+                loadK(st, u, ka2);
+            }
             // A operand of O^T += V^T P^T over 32 keys: lane l holds keys
             // 4 kb .. 4 kb + 3 of both sub-tiles (k-slots 8 kb .. 8 kb + 7)
             vec4 va[DS];
@@ -1794,15 +1819,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                 const vec2 l2 = __builtin_bit_cast(vec2, lo), h2 = __builtin_bit_cast(vec2, hi);
                 va[d] = vec4{l2.x, l2.y, h2.x, h2.y};
             }
-            const bool masked = key0 + 31 > mask_free;  // wave-uniform
-            // K operands of both sub-tiles, requested together (the second
-            // sub-tile's rows are in LDS whether or not they are used)
-            vec4 ka2[2][KL];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int i = 0; i < KL; ++i)
-                    ka2[hh][i] = *reinterpret_cast<const vec4 *>(kt + hh * 16 * ROWB + koff[i]);
             // The four score chains (2 sub-tiles x NQ column tiles) advance
             // together, so consecutive products never depend on each other.
             float4_t sc[2][NQ];
@@ -1816,6 +1832,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                     for (int c = 0; c < NQ; ++c) sc[hh][c] = M::qk(ka2[hh][i], qb[c][i], sc[hh][c]);
+            if (pre) loadK(st, u + 2, knext);  // the next pair's K, in flight under this softmax
             // Keys past the wave's last row (all of the second sub-tile when
             // key0 + 16 > w_last) are hidden by the causal mask below, which
             // applies whenever that holds (mask_free <= w_last).
@@ -1906,8 +1923,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
             if (j + 1 < nst) issue(j + 1, st ^ 1);
             const int key0 = ck0 + KT * j;
             if (key0 > w_last) return;  // wave-uniform: the whole tile is past this wave's rows
-            pair(st, 0, key0);
-            if (key0 + 32 <= w_last) pair(st, 2, key0 + 32);
+            const bool two = key0 + 32 <= w_last;
+            pair(st, 0, key0, false, two);
+            if (two) pair(st, 2, key0 + 32, true, false);
         };
         issue(0, 0);
         for (int j = 0; j < nst; j += 2) {
