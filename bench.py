@@ -181,6 +181,9 @@ def paged_dense_ratio(points, rounds=15, warm=3):
     return res
 
 
+SETTLE_SCALE = 1.0  # --settle: 0 times each leg from a cold start (counter passes)
+
+
 def settle(run_once, seconds):
     """Repeat run_once() (GPU work, synchronized after each call) for
     ``seconds`` of wall time before a leg is timed, so that the GPU runs at
@@ -189,8 +192,10 @@ def settle(run_once, seconds):
     or more of work."""
     import torch
 
+    run_once()  # at least once: the first launches also page in code and data
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < seconds * SETTLE_SCALE:
         run_once()
         torch.cuda.synchronize()
 
@@ -1090,6 +1095,9 @@ def main():
     # 500 untimed steps (~43 ms): after 20 the timed region read ~1.5% slower
     # than after 500 or 2000, the GPU still settling into sustained load
     ap.add_argument("--warmup", type=int, default=500)
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="scale of the time each leg runs before it is timed (0: none; for "
+                         "counter passes, which profile every launch)")
     ap.add_argument("--partition", type=int, default=0,
                     help="split-K partition size for pa_decode (0 = none)")
     ap.add_argument("--replicas", type=int, default=4,
@@ -1115,6 +1123,8 @@ def main():
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
                     help="write profile summaries from rocprofv3 CSV output (no GPU needed)")
     args = ap.parse_args()
+    global SETTLE_SCALE
+    SETTLE_SCALE = max(0.0, args.settle)
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, commands=PROFILE_COMMANDS)
         return
