@@ -220,6 +220,8 @@ struct DecodeArgs {
     const int32_t *group_shared;
     int32_t *skip_out;
     int32_t Gh, Pg;
+    int32_t hg;         // kv heads per workgroup (VALU kernel: 1 or 2)
+    int32_t ips;        // workgroup items per sequence (Hkv / hg)
     int32_t rank;       // 1: longest-first sequence order (S <= kRankMaxSeqs)
     int32_t spec_blocks;  // table entries a partition can need (fetched before its length)
     int64_t tok_bytes;  // bytes between consecutive tokens of one head
@@ -330,7 +332,7 @@ __device__ __forceinline__ void grid_pos(const DecodeArgs &a, int &item, int &pa
 template <int MODE>
 __device__ void pick_work(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, int32_t *s_tab,
                           int item, int part, int tid, int nt_, int &s, int &n, bool &staged) {
-    const int want = item / a.Hkv;
+    const int want = item / a.ips;
     staged = false;
     if (a.rank) {
         s = rank_pick(a, s_len, s_pick, want, tid, nt_);
@@ -350,25 +352,26 @@ __device__ void pick_work(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, 
 // End of a decode workgroup: combine the waves' running states (red[w][g] =
 // acc[0..D), m, l) and store either the output row (a single partition
 // covers the sequence) or the partition's unnormalised partial, which the
-// merge kernel combines.
+// merge kernel combines.  hg kv heads per workgroup, nw waves each (head k's
+// waves are k nw .. k nw + nw - 1; its query rows follow head k - 1's).
 template <typename T, int D, int G>
-__device__ void finish_workgroup(const DecodeArgs &a, const float *red, int nw, int64_t qrow0,
-                                 int part, int n, int tid, int nthr) {
+__device__ void finish_workgroup(const DecodeArgs &a, const float *red, int nw, int hg,
+                                 int64_t qrow0, int part, int n, int tid, int nthr) {
     const bool direct = a.PS == 0 || n <= a.PS;
-    for (int i = tid; i < G * D; i += nthr) {
-        const int g = i / D, d = i % D;
+    for (int i = tid; i < hg * G * D; i += nthr) {
+        const int k = i / (G * D), ri = i - k * (G * D);
+        const int g = ri / D, d = ri % D;
+        const float *rk = red + k * nw * G * (D + 2);
         float M = kNegBig;
-#pragma unroll
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, red[(w * G + g) * (D + 2) + D]);
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, rk[(w * G + g) * (D + 2) + D]);
         float L = 0.0f, A = 0.0f;
-#pragma unroll
         for (int w = 0; w < nw; ++w) {
-            const float *r = red + (w * G + g) * (D + 2);
+            const float *r = rk + (w * G + g) * (D + 2);
             const float cw = fexp2(r[D] - M);
             L = fmaf(r[D + 1], cw, L);
             A = fmaf(r[d], cw, A);
         }
-        const int64_t qh = qrow0 + g;
+        const int64_t qh = qrow0 + k * G + g;
         if (direct) {
             Elem<T>::store(a.out, qh * D + d, A / L);
         } else {
@@ -445,14 +448,22 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int rg = lane / LPR;   // row group
     const int c = lane % LPR;    // 16-byte chunk of the row
+    // With hg = 2 a workgroup serves two adjacent kv heads of one sequence,
+    // nw / 2 waves each: on a token-major pool their rows of a token are
+    // adjacent, so the two halves read 512 contiguous bytes per token.
+    const int hg = a.hg;
+    const int nwh = nw >> (hg - 1);       // waves per kv head (2, 4 or 8)
+    const int lwh = 31 - __builtin_clz(nwh);
+    const int sub = wave >> lwh;          // this wave's kv head within the workgroup
+    const int wh = wave & (nwh - 1);      // its index among that head's waves
     int item, part;
     grid_pos(a, item, part);
-    const int h = item % a.Hkv;
+    const int h = (item % a.ips) * hg + sub;
     // Leading partitions of a shared prefix are the grouped launch's (its
     // count is requested first, so a workgroup with nothing to do leaves
     // after one round trip; no ranking with a shared prefix, so the
     // sequence is item / Hkv).
-    const int skip_s = a.skip ? a.skip[item / a.Hkv] : 0;
+    const int skip_s = a.skip ? a.skip[item / a.ips] : 0;
 
     int s, n;
     bool staged;
@@ -461,6 +472,7 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     const int tb = a.PS ? part * a.PS : 0;
     const int te = a.PS ? min(n, tb + a.PS) : n;
     const int64_t qrow0 = (int64_t)s * a.Hq + (int64_t)h * G;  // first query head of the group
+    const int64_t qrow_wg = qrow0 - (int64_t)sub * G;          // the workgroup's first query head
 
     // q for the G heads of the group: this lane's 16-byte chunk, unscaled
     // (issued before the length test so it overlaps the other first loads).
@@ -469,12 +481,12 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     for (int g = 0; g < G; ++g)
         qv[g] = load_cached(a.q + ((qrow0 + g) * D + (int64_t)c * EPL) * sizeof(T));
     // Append mode: the workgroup whose range ends at n takes position n - 1
-    // from k_new / v_new after the loop (wave 0), so the loop stops before it;
+    // from k_new / v_new after the loop (the head's first wave), so the loop stops before it;
     // its 16-byte pieces are requested here, with q.
     const bool app = MODE != kDense && a.k_new != nullptr && te == n;
     const uint32_t chunk_off = (uint32_t)(c * EPL * (int)sizeof(T));
     vec4 kn = {}, vn = {};
-    if (app && wave == 0 && tb < te) {
+    if (app && wh == 0 && tb < te) {
         const int64_t nsrc = ((int64_t)s * a.Hkv + h) * D * (int64_t)sizeof(T) + chunk_off;
         kn = load_cached(a.k_new + nsrc);
         vn = load_cached(a.v_new + nsrc);
@@ -483,7 +495,7 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     if (tb >= te) {
         // Only an empty sequence reaches here with part == 0: its row is zero.
         if (part == 0)
-            for (int i = tid; i < G * D; i += nthr) E::store(a.out, qrow0 * D + i, 0.0f);
+            for (int i = tid; i < hg * G * D; i += nthr) E::store(a.out, qrow_wg * D + i, 0.0f);
         return;
     }
 
@@ -599,8 +611,9 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
             }
         };
 
-        // Steps: wave w takes steps w, w + 4, ... of the nst steps, the
-        // partly filled last one (index nfull, if any) included.  The next
+        // Steps: the wave with index wh among its head's nwh waves takes
+        // steps wh, wh + nwh, ... of the nst steps, the partly filled last
+        // one (index nfull, if any) included.  The next
         // step's loads are always issued before the current step is
         // computed, so exactly one step of loads is outstanding while a step
         // is computed, the partly filled one too.  Only the last step of a
@@ -621,23 +634,23 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
                 compute.template operator()<true>(kb, vb, jj);
         };
         vec4 ka[U], va[U], kb2[U], vb2[U];
-        int j = wave;
+        int j = wh;
         if (j < nst) {
             issue_any(ka, va, j);
-            while (j + 2 * nw < nst) {
-                issue.template operator()<false>(kb2, vb2, j + nw);   // j + nw < nst - nw <= nfull
+            while (j + 2 * nwh < nst) {
+                issue.template operator()<false>(kb2, vb2, j + nwh);   // j + nwh < nst - nwh <= nfull
                 __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
                 compute.template operator()<false>(ka, va, j);
-                issue_any(ka, va, j + 2 * nw);
+                issue_any(ka, va, j + 2 * nwh);
                 __builtin_amdgcn_sched_barrier(0);
-                compute.template operator()<false>(kb2, vb2, j + nw);
-                j += 2 * nw;
+                compute.template operator()<false>(kb2, vb2, j + nwh);
+                j += 2 * nwh;
             }
-            if (j + nw < nst) {
-                issue_any(kb2, vb2, j + nw);
+            if (j + nwh < nst) {
+                issue_any(kb2, vb2, j + nwh);
                 __builtin_amdgcn_sched_barrier(0);
-                compute.template operator()<false>(ka, va, j);      // j < j + nw <= nfull
-                compute_last(kb2, vb2, j + nw);
+                compute.template operator()<false>(ka, va, j);      // j < j + nwh <= nfull
+                compute_last(kb2, vb2, j + nwh);
             } else {
                 compute_last(ka, va, j);
             }
@@ -663,8 +676,8 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
         }
     }
 
-    if (app && wave == 0) {
-        // Every row group of wave 0 now holds the wave's merged state: add
+    if (app && wh == 0) {
+        // Every row group of the head's first wave now holds the wave's merged state: add
         // position n - 1 as one more online-softmax step, and store its rows
         // in their slot (lanes 0 .. LPR - 1 hold the whole row).
         float vf[EPL];
@@ -699,7 +712,7 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
         }
     }
     __syncthreads();
-    finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
+    finish_workgroup<T, D, G>(a, red, nwh, hg, qrow_wg, part, n, tid, nthr);
 }
 
 // ---------------------------------------------------------------- grouped-query decode on MFMA
@@ -1107,7 +1120,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     if constexpr (GROUPED)
         finish_group<T, D>(a, red, nw, G, s, h, part, cols, s_len, tid, nthr);
     else
-        finish_workgroup<T, D, G>(a, red, nw, qrow0, part, n, tid, nthr);
+        finish_workgroup<T, D, G>(a, red, nw, 1, qrow0, part, n, tid, nthr);
 }
 
 // Combines the partitions of one (sequence, query head): with M the largest
@@ -1365,6 +1378,8 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.skip_out = nullptr;
     a.Gh = l.Hq / l.Hkv;
     a.Pg = 1;
+    a.hg = 1;
+    a.ips = l.Hkv;
     // Ranking costs the workgroup one dependent round trip; it pays only when
     // the grid is too large to be resident at once, so that order matters.
     a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512) ? 1 : 0;
@@ -1417,6 +1432,22 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
         const void *ref = (const void *)decode_kernel<T, D, G, kPagedWide>;
         nw = pick_waves(max_waves<T>() >= 8 ? ref : nullptr, ref, wgs, lds_of(8), lds_of(4));
         lds = lds_of(nw);
+        // Token-major pools keep a token's kv heads side by side: on grids of
+        // at least two rounds of 4-wave workgroups, two adjacent kv heads
+        // share an 8-wave workgroup (4 waves each, the same split of the
+        // work, so the same bits), and their rows of a token are read
+        // together (OPT-13B batch: 85.7 against 88.6 us; 128 x 64: 47.8
+        // against 53.5; 128 x 2048: 831 against 859).  On 1.25 rounds (32
+        // sequences x 40 heads) it was 3-7% slower, and on head-major pools,
+        // where the two heads' rows are 4 KiB apart, 1% slower.
+        if (l.layout == 0 && nw == 4 && max_waves<T>() >= 8 && l.Hkv % 2 == 0 &&
+            l.n_groups == 0 && wgs >= 2 * resident_workgroups(ref, 4, lds_of(4))) {
+            a.hg = 2;
+            a.ips = l.Hkv / 2;
+            nw = 8;
+            lds = lds_of(8);
+            grid = dim3((unsigned)((int64_t)l.S * a.ips * l.P), 1, 1);
+        }
     }
     (void)hipGetLastError();  // an error left by other code is not this launch's
     if (l.n_groups > 0) {
