@@ -1296,6 +1296,84 @@ __global__ __launch_bounds__(kMergeThreads) void merge_rows_kernel(
     Elem<T>::store(out, o + 3, a.w / L);
 }
 
+// Four consecutive output elements in one store, each rounded as
+// Elem<T>::store rounds it (the index is a multiple of 4 and the row start
+// 16-byte aligned, so the store is aligned).
+template <typename T>
+__device__ __forceinline__ void store4(void *out, int64_t i, float x0, float x1, float x2, float x3) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<float4 *>((float *)out + i) = make_float4(x0, x1, x2, x3);
+    } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<t4 *>((T *)out + i) = t4{(T)x0, (T)x1, (T)x2, (T)x3};
+    }
+}
+
+// The same combination with one wave per (sequence, query head) and up to
+// kMergeWaveRegs partitions per lane: lane l takes the 4-float chunk
+// l % (D/4) of the row and partitions l / (D/4), l / (D/4) + NG, ... (NG =
+// 64 / (D/4) lane groups), all requested at once together with the length
+// (addresses clamped to the P allocated partitions); the largest partition
+// max and the group sums are combined by lane exchanges, so there is no LDS
+// and no barrier, and each chunk leaves in one store.  The sum runs in a
+// fixed order (partition order inside a lane, then the groups' butterfly).
+constexpr int kMergeWaveRegs = 16;
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void merge_wave_kernel(
+    const float *ws_acc, const float *ws_ml, const int32_t *lens, void *out, int32_t Hq, int32_t P,
+    int32_t PS, int32_t max_ctx) {
+    constexpr int C4 = D / 4;       // float4 chunks per row
+    constexpr int NG = 64 / C4;     // lane groups (2 for D 128, 4 for D 64)
+    const int64_t qh = blockIdx.x;  // s * Hq + h
+    const int lane = threadIdx.x;
+    const int c = lane % C4, grp = lane / C4;
+    const float *ml = ws_ml + qh * P * 2;
+    const float4 *ac = reinterpret_cast<const float4 *>(ws_acc + qh * P * D);
+    float mp[kMergeWaveRegs], lp[kMergeWaveRegs];
+    float4 x[kMergeWaveRegs];
+#pragma unroll
+    for (int k = 0; k < kMergeWaveRegs; ++k) {
+        int pc = grp + k * NG;
+        pc = pc < P ? pc : P - 1;
+        mp[k] = ml[2 * pc];
+        lp[k] = ml[2 * pc + 1];
+        x[k] = ac[(int64_t)pc * C4 + c];
+    }
+    const int n = clamp_len(lens[qh / Hq], max_ctx);
+    const int np = (n + PS - 1) / PS;
+    if (np <= 1) return;  // written by the decode kernel
+    float M = kNegBig;
+#pragma unroll
+    for (int k = 0; k < kMergeWaveRegs; ++k) M = grp + k * NG < np ? fmaxf(M, mp[k]) : M;
+#pragma unroll
+    for (int off = C4; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMergeWaveRegs; ++k) {
+        if (grp + k * NG < np) {
+            const float w = fexp2(mp[k] - M);
+            a.x = fmaf(x[k].x, w, a.x);
+            a.y = fmaf(x[k].y, w, a.y);
+            a.z = fmaf(x[k].z, w, a.z);
+            a.w = fmaf(x[k].w, w, a.w);
+            L = fmaf(lp[k], w, L);
+        }
+    }
+    // Butterfly over the groups: every lane of a chunk ends with the same
+    // bits (each step adds two equal-valued operands in swapped order).
+#pragma unroll
+    for (int off = C4; off < 64; off <<= 1) {
+        a.x += __shfl_xor(a.x, off, 64);
+        a.y += __shfl_xor(a.y, off, 64);
+        a.z += __shfl_xor(a.z, off, 64);
+        a.w += __shfl_xor(a.w, off, 64);
+        L += __shfl_xor(L, off, 64);
+    }
+    if (grp == 0) store4<T>(out, qh * D + 4 * c, a.x / L, a.y / L, a.z / L, a.w / L);
+}
+
 // Workgroups of one kernel that a CU holds at once, at a given block size and
 // dynamic LDS, times the CU count of the current device.  Queried once per
 // (kernel, waves, device) and cached; the query itself is host-only.
@@ -1492,6 +1570,9 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
         hipLaunchKernelGGL((merge_rows_kernel<T, D>), dim3((unsigned)((rows + RPW - 1) / RPW)),
                            dim3(kMergeThreads), 0, st, a.ws_acc, a.ws_ml, l.lens, l.out,
                            (int32_t)rows, l.Hq, l.P, l.PS, l.max_ctx);
+    } else if (l.P <= kMergeWaveRegs * (64 / (D / 4))) {
+        hipLaunchKernelGGL((merge_wave_kernel<T, D>), dim3((unsigned)rows), dim3(64), 0, st,
+                           a.ws_acc, a.ws_ml, l.lens, l.out, l.Hq, l.P, l.PS, l.max_ctx);
     } else {
         hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)rows), dim3(kMergeThreads), 0, st,
                            a.ws_acc, a.ws_ml, l.lens, l.out, l.Hq, l.P, l.PS, l.max_ctx);
