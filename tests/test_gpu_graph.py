@@ -6,17 +6,20 @@ pa_cache_write (the new tokens), pa_decode (split-K and merge, or not),
 pa_decode_append on a second pool, and pa_prefill.  Between replays eager
 work poisons every output and every location the graph writes (NaN), with
 synchronisations in between; each replay must then give, bit for bit, what
-the same calls give eagerly.  The library issues kernel launches only (no
-memsets, copies or allocations), so a graph holds exactly its kernels.
+the same calls give eagerly, and what the fp64 oracle computes for the same
+iteration (pools bit-exact, attention outputs within the stated tolerance).
+The library issues kernel launches only (no memsets, copies or
+allocations), so a graph holds exactly its kernels.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
+import oracle
 import workloads as W
-from gpu_util import in_layout, to_dev, to_host, torch_dtype
-from helpers import same_bits
+from gpu_util import f64, in_layout, to_dev, to_host, torch_dtype
+from helpers import assert_fp_close, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -36,10 +39,26 @@ def _newest_slots(p):
                      for s, n in enumerate(p.context_lens)], np.int32)
 
 
+def _oracle_iteration(p, layout, dtype, pairs, kn, vn, slots, qp, qs):
+    """The iteration below computed by the oracle: pools and outputs."""
+    k0, v0 = in_layout(p.k_cache, layout), in_layout(p.v_cache, layout)
+    k1, v1 = oracle.copy_blocks(k0, v0, pairs, dtype, layout=layout)
+    k, v = oracle.cache_write(kn, vn, k1, v1, slots, dtype, layout=layout)
+    out = oracle.decode(p.q, k, v, p.block_tables, p.context_lens, p.scale, dtype, layout=layout)
+    k2, v2 = oracle.cache_write(kn, vn, k0, v0, slots, dtype, layout=layout)
+    out2 = oracle.decode(p.q, k2, v2, p.block_tables, p.context_lens, p.scale, dtype,
+                         layout=layout)
+    res = dict(k=k, v=v, k2=k2, v2=v2, out=out, out2=out2)
+    if dtype != "f32":
+        res["outp"] = oracle.prefill(qp, k, v, p.block_tables, p.context_lens, qs, p.scale,
+                                     dtype, layout=layout)
+    return res
+
+
 @pytest.mark.parametrize("dtype,hq,hkv", [("f16", 8, 8), ("bf16", 12, 2), ("f32", 4, 2)])
 @pytest.mark.parametrize("ps", [0, 64])
 @pytest.mark.parametrize("layout", ["NHD", "HND"])
-def test_iteration_graph_replays_match_eager(dtype, hq, hkv, ps, layout):
+def test_iteration_graph_replays_match_eager_and_oracle(dtype, hq, hkv, ps, layout):
     import torch
 
     import paged_kv_cache_pa_amd as pa
@@ -94,6 +113,7 @@ def test_iteration_graph_replays_match_eager(dtype, hq, hkv, ps, layout):
     torch.cuda.synchronize()
     skip = {"ws"} | ({"outp"} if dtype == "f32" else set())
     want = {name: to_host(t, dtype) for name, t in ref.items() if name not in skip}
+    expect = _oracle_iteration(p, layout, dtype, pairs, kn, vn, slots, qp, qs)
 
     # capture (after one eager call on a side stream, so every lazily
     # initialised piece of state exists before the capture starts)
@@ -124,4 +144,9 @@ def test_iteration_graph_replays_match_eager(dtype, hq, hkv, ps, layout):
         graph.replay()
         torch.cuda.synchronize()
         for name, w in want.items():
-            assert same_bits(to_host(g_buf[name], dtype), w), (replay, name)
+            got = to_host(g_buf[name], dtype)
+            assert same_bits(got, w), (replay, name)
+            if name in ("k", "v", "k2", "v2"):
+                assert same_bits(got, expect[name]), (replay, name, "oracle")
+            else:
+                assert_fp_close(f64(got, dtype), expect[name], dtype, f"replay {replay} {name}")
