@@ -1771,13 +1771,6 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
 #pragma unroll
             for (int i = 0; i < KL; ++i) qb[c][i] ^= vec4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
     }
-    // The q loads complete here: a wait for them must not fall inside the key
-    // loop, where it would also wait for the LDS DMA in flight.
-#pragma unroll
-    for (int c = 0; c < NQ; ++c)
-#pragma unroll
-        for (int i = 0; i < KL; ++i) asm volatile("" ::"v"(qb[c][i]));
-
     // Running max m (raw units) per query column, and the two values derived
     // from it that the loop uses: thr = m + 2^kLazy-in-raw-units (a score
     // above it moves the max) and nms = -s m.  The start value is finite and
@@ -1835,6 +1828,14 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
         const int mask_free = min(mask_free_rows, ck1 - 1);
         __syncthreads();  // the previous chunk's readers are done
         stage_table(trow, cb, cn, a.NB, s_tab, tid, blockDim.x);
+        // The q loads complete here, with the first chunk's table entries
+        // (their round trips overlap; on later chunks this is a no-op): a
+        // wait for q must not fall inside the key loop, where it would also
+        // wait for the LDS DMA in flight.
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+#pragma unroll
+            for (int i = 0; i < KL; ++i) asm volatile("" ::"v"(qb[c][i]));
         __syncthreads();
 
         // DMA of tile j (keys clamped to the chunk, so rows past its end
@@ -2047,6 +2048,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64, 2) void prefill_kernel(PrefillA
         }
     }
 
+    // (q was consumed in the loop; consuming it here too tells the compiler
+    // so on every path, and keeps its waits out of the stores below.)
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+#pragma unroll
+        for (int i = 0; i < KL; ++i) asm volatile("" ::"v"(qb[c][i]));
     // Every lane of a query column holds the column's full weight sum.
 #pragma unroll
     for (int c = 0; c < NQ; ++c) {
