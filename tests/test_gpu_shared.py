@@ -204,3 +204,74 @@ def test_deterministic_and_no_groups():
     torch.cuda.synchronize()
     plain = run_decode(p, partition_size=32, tensors=t, layout="HND")
     assert same_bits(to_host(out, "f16"), plain)
+
+
+def test_back_to_back_calls_and_graph_replays():
+    """The grouped pass runs on a second stream beside the caller's: calls
+    issued back to back on one stream with one shared workspace (no
+    synchronisation between them) must each see only their own partials, on
+    the default stream and on another one; and the call captured in a HIP
+    graph must replay, after eager NaN poisoning of its output, with the
+    eager call's bits (and the oracle's values) every time."""
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    p, gs, gsh = W.random_shared(94, "f16", [(8, [140, 150, 160, 170]), (4, [70, 90]), (0, [33])],
+                                 4, 4, 128)
+    rng = np.random.default_rng(95)
+    q2 = W.randn(rng, p.q.shape, "f16")
+    ref1 = oracle.decode(p.q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, "f16")
+    ref2 = oracle.decode(q2, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, "f16")
+    q, k, v, bt, cl = upload(p, "HND")
+    qb = to_dev(q2, "f16")
+    gs_d, gsh_d = to_dev(gs), to_dev(gsh)
+    mcl = int(p.context_lens.max())
+    ps = 32
+    S, Hq, D = p.q.shape
+    P = -(-mcl // ps)
+    ws = torch.full((S * Hq * P * (D + 2) + S + 64,), float("nan"), dtype=torch.float32,
+                    device=q.device)
+
+    def call(qq, out, stream=None):
+        pa.pa_decode_shared(qq, k, v, bt, cl, gs_d, gsh_d, p.scale, out,
+                            max_shared_blocks=int(gsh.max()), max_context_len=mcl,
+                            partition_size=ps, workspace=ws, layout="HND", stream=stream)
+
+    torch.cuda.synchronize()   # the inputs are ready for any stream
+    first = None
+    for stream in (None, torch.cuda.Stream()):
+        with torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(
+                torch.cuda.current_stream()):
+            outs = [empty_out(p) for _ in range(4)]
+            for i, o in enumerate(outs):   # q, q2, q, q2 back to back
+                call(q if i % 2 == 0 else qb, o)
+        torch.cuda.synchronize()
+        got = [to_host(o, "f16") for o in outs]
+        assert_fp_close(f64(got[0], "f16"), ref1, "f16", "back to back, first")
+        assert_fp_close(f64(got[1], "f16"), ref2, "f16", "back to back, second")
+        assert same_bits(got[0], got[2]) and same_bits(got[1], got[3]), "back to back: repeat differs"
+        if first is None:
+            first = got[0]
+        assert same_bits(got[0], first), "default stream vs another stream"
+
+    out = empty_out(p)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(q, out)          # one eager call on the capture stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(q, out)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(out, "f16")
+        assert same_bits(got, first), f"replay {replay} differs from the eager call"
+        assert_fp_close(f64(got, "f16"), ref1, "f16", f"replay {replay}")
