@@ -207,12 +207,12 @@ def test_deterministic_and_no_groups():
 
 
 def test_back_to_back_calls_and_graph_replays():
-    """The grouped pass runs on a second stream beside the caller's: calls
-    issued back to back on one stream with one shared workspace (no
-    synchronisation between them) must each see only their own partials, on
-    the default stream and on another one; and the call captured in a HIP
-    graph must replay, after eager NaN poisoning of its output, with the
-    eager call's bits (and the oracle's values) every time."""
+    """Calls issued back to back on one stream with one shared workspace (no
+    synchronisation between them) each see only their own partials, on the
+    default stream and on another one; and the call (grouped pass, usual
+    pass, merge) captured in a HIP graph replays, after eager NaN poisoning
+    of its output and workspace, with the eager call's bits and the
+    oracle's values every time."""
     import torch
 
     import paged_kv_cache_pa_amd as pa
