@@ -128,3 +128,40 @@ def test_split_equals_dense_split():
     torch.cuda.synchronize()
     assert same_bits(to_host(out, "bf16"), got)
     check(p, got, "ragged bf16 G 6")
+
+
+# Partition counts at the edges of the merge forms: up to 8 partitions one
+# thread per row chunk (merge_rows_kernel), then one wave per row up to 32
+# (head dim 128) or 64 (head dim 64) partitions, then a 256-thread
+# workgroup per row.  The longest sequence has exactly P partitions; the
+# others end inside the first, the middle and the last of them.
+MERGE_EDGES = [
+    # (label, dtype, D, P)
+    ("8 partitions, head dim 128", "f16", 128, 8),
+    ("9 partitions, head dim 128", "bf16", 128, 9),
+    ("32 partitions, head dim 128", "f16", 128, 32),
+    ("33 partitions, head dim 128", "bf16", 128, 33),
+    ("64 partitions, head dim 64", "f16", 64, 64),
+    ("65 partitions, head dim 64", "bf16", 64, 65),
+]
+
+
+@pytest.mark.parametrize("label,dtype,d,P", MERGE_EDGES, ids=[m[0] for m in MERGE_EDGES])
+def test_merge_form_edges(label, dtype, d, P):
+    import torch
+
+    import paged_kv_cache_pa_amd as pa
+
+    ps = 16
+    lens = [P * ps, P * ps - 5, 9, (P // 2) * ps + 1, 0, ps + 1]
+    p = W.random_paged(907 + P, dtype, lens, 8, 2, d)
+    print(label, flush=True)
+    S, Hq, D = p.q.shape
+    params = pa.DecodeParams(S, Hq, p.num_kv_heads, D, p.block_size, p.max_blocks_per_seq,
+                             p.num_blocks, int(p.context_lens.max()), ps,
+                             {"f32": 0, "f16": 1, "bf16": 2}[dtype], pa.LAYOUTS["HND"])
+    ws = torch.full((pa.pa_decode_workspace_size(params) // 4,), float("nan"),
+                    dtype=torch.float32, device="cuda")
+    got = run(p, ps, ws, "HND")
+    check(p, got, label)
+    assert (f64(got, dtype)[4] == 0).all(), "the empty sequence's rows are zero"
