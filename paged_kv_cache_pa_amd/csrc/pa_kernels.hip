@@ -68,6 +68,7 @@ constexpr int kMaxWaves = 8;        // decode workgroups have 4 or 8 waves (chos
 constexpr int kStepTokens = 16;     // tokens per wave step
 constexpr int kTableChunk = 1024;   // block-table entries staged in LDS at once
 constexpr int kRankMaxSeqs = 256;   // longest-first scheduling up to this batch
+constexpr int kRankMinCtx = 64;     // ... and only above this max_context_len
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.402823466e38f;  // running-max start (finite)
 
@@ -257,12 +258,21 @@ __device__ int rank_pick(const DecodeArgs &a, int32_t *s_len, int32_t *s_pick, i
     const int t = tid / k, j = tid % k;
     if (t < a.S) {
         const int nt = s_len[t];
-        const int per = (a.S + k - 1) / k;
+        // Each lane's part starts at a multiple of 4 and is read four
+        // lengths per 16-byte LDS read, several reads in flight (one read
+        // per length, each waited for, cost ~100 cycles a length); entries
+        // past the part are masked out by index.
+        const int per = ((a.S + k - 1) / k + 3) & ~3;
         const int u0 = j * per, u1 = min(a.S, u0 + per);
+        const int4 *l4 = reinterpret_cast<const int4 *>(s_len);
+        auto longer = [&](int nu, int u) {
+            return (int)((u < u1) & ((nu > nt) | ((nu == nt) & (u < t))));
+        };
         int r = 0;
-        for (int u = u0; u < u1; ++u) {
-            const int nu = s_len[u];
-            r += (nu > nt) | ((nu == nt) & (u < t));
+#pragma unroll 4
+        for (int u = u0; u < u1; u += 4) {
+            const int4 L = l4[u >> 2];
+            r += longer(L.x, u) + longer(L.y, u + 1) + longer(L.z, u + 2) + longer(L.w, u + 3);
         }
         for (int off = 1; off < k; off <<= 1) r += __shfl_xor(r, off, 64);
         if (j == 0 && r == want) *s_pick = t;
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(max_waves<T>() * 64) void decode_kernel(DecodeArgs 
     // loop, then the cross-wave merge buffer [waves][G][D + 2].
     extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
     float *smem = reinterpret_cast<float *>(dyn_smem);
-    __shared__ int32_t s_len[kRankMaxSeqs];
+    __shared__ __attribute__((aligned(16))) int32_t s_len[kRankMaxSeqs];
     __shared__ int32_t s_pick;
     int32_t *s_tab = reinterpret_cast<int32_t *>(smem);
 
@@ -837,7 +847,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_mma_kernel(DecodeArgs a
     // V tile per wave during the loop, then the cross-wave merge buffer.
     extern __shared__ __attribute__((aligned(16))) char dyn_smem[];
     char *smem = dyn_smem;
-    __shared__ int32_t s_len[kRankMaxSeqs];
+    __shared__ __attribute__((aligned(16))) int32_t s_len[kRankMaxSeqs];
     __shared__ int32_t s_pick;
     int32_t *s_tab = reinterpret_cast<int32_t *>(smem);
 
@@ -1459,8 +1469,11 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.hg = 1;
     a.ips = l.Hkv;
     // Ranking costs the workgroup one dependent round trip; it pays only when
-    // the grid is too large to be resident at once, so that order matters.
-    a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512) ? 1 : 0;
+    // the grid is too large to be resident at once, so that order matters,
+    // and when a sequence can hold more than kRankMinCtx tokens: items of at
+    // most four 16-token steps differ by less than that round trip costs.
+    a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512 &&
+              l.max_ctx > kRankMinCtx) ? 1 : 0;
     {
         const int64_t span = l.PS ? (l.PS < l.max_ctx ? l.PS : l.max_ctx) : l.max_ctx;
         a.spec_blocks = (int32_t)((span + B - 1) / B);
