@@ -40,11 +40,12 @@
 //    never on where blocks sit, so paged and dense results are bitwise equal
 //    and invariant to block placement.
 //  * Scheduling: for unsplit launches of up to 256 sequences with more than
-//    512 (sequence, kv head) items (more than the chip holds at once), every
-//    workgroup ranks the sequences by context length (longest first, ties
-//    by index) and takes the sequence whose rank matches its grid position,
-//    so the longest sequences start first and the tail of the launch is
-//    short.  Which workgroup computes a row never changes its arithmetic.
+//    512 (sequence, kv head) items (more than the chip holds at once) and
+//    contexts that may exceed 64 tokens, every workgroup ranks the
+//    sequences by context length (longest first, ties by index) and takes
+//    the sequence whose rank matches its grid position, so the longest
+//    sequences start first and the tail of the launch is short.  Which
+//    workgroup computes a row never changes its arithmetic.
 //  * Split-K: partition p covers tokens [p*PS, (p+1)*PS) and writes its
 //    unnormalised partial (acc, m, l) to the workspace; a merge kernel then
 //    combines the partitions by the log-sum-exp identity ([Int] "The kernel
