@@ -408,6 +408,10 @@ def test_batch_sizes_and_scheduling(S):
     ("bf16", 200, 16, 4, 128),   # matrix-core kernel (G 4), 800 workgroups
     ("f32", 130, 8, 4, 64),      # VALU kernel with G 2, 520 workgroups
     ("f16", 256, 3, 3, 128),     # VALU kernel, MHA, 768 workgroups, 256 sequences
+    # up to 64 sequences every wave ranks on its own
+    ("f16", 64, 16, 16, 128),    # VALU kernel, MHA, 1024 workgroups
+    ("bf16", 33, 64, 16, 64),    # matrix-core kernel (G 4), 528 workgroups
+    ("f16", 2, 300, 300, 64),    # two sequences, 600 workgroups
 ])
 def test_longest_first_order_every_kernel(dtype, S, hq, hkv, d):
     """Longest-first order (more than 512 workgroups, at most 256 sequences,
