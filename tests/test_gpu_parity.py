@@ -468,3 +468,25 @@ def test_binding_refuses_mismatched_head_dim():
     qs = torch.tensor([0, 1, 2], dtype=torch.int32, device=dev)
     with pytest.raises(ValueError, match="head dim"):
         pa.pa_prefill(q, k, k, bt, cl, qs, 1.0, out)
+
+
+@pytest.mark.parametrize("dtype,hq,hkv", [("f16", 16, 16), ("bf16", 64, 16)])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_order_does_not_change_bits(dtype, hq, hkv, layout):
+    """The same batch (every context at most 64 tokens, more than 512
+    workgroups) decoded without longest-first order (max_context_len 64)
+    and with it (max_context_len 65, the same clamped lengths): which
+    workgroup computes a row never changes its arithmetic, so the bits are
+    equal, and both match the oracle."""
+    rng = np.random.default_rng(4200 + hq)
+    S = 64
+    lens = rng.integers(0, 65, size=S)
+    lens[::9] = 64
+    lens[4::11] = 0
+    lens[6::13] = 1
+    p = W.random_paged(4300 + hq, dtype, lens, hq, hkv, 128, extra_blocks=2, mbs=5)
+    t = upload(p, layout)
+    plain = run_decode(p, max_context_len=64, tensors=t, layout=layout)
+    ranked = run_decode(p, max_context_len=65, tensors=t, layout=layout)
+    assert same_bits(plain, ranked), f"{dtype} {layout}: order changed the bits"
+    check(p, ranked, ref_decode(p), f"order {dtype} {layout}")
