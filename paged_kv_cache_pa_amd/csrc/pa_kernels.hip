@@ -40,12 +40,11 @@
 //    never on where blocks sit, so paged and dense results are bitwise equal
 //    and invariant to block placement.
 //  * Scheduling: for unsplit launches of up to 256 sequences with more than
-//    512 (sequence, kv head) items (more than the chip holds at once) and
-//    contexts that may exceed 64 tokens, every workgroup ranks the
-//    sequences by context length (longest first, ties by index) and takes
-//    the sequence whose rank matches its grid position, so the longest
-//    sequences start first and the tail of the launch is short.  Which
-//    workgroup computes a row never changes its arithmetic.
+//    512 (sequence, kv head) items (more than the chip holds at once), every
+//    workgroup ranks the sequences by context length (longest first, ties
+//    by index) and takes the sequence whose rank matches its grid position,
+//    so the longest sequences start first and the tail of the launch is
+//    short.  Which workgroup computes a row never changes its arithmetic.
 //  * Split-K: partition p covers tokens [p*PS, (p+1)*PS) and writes its
 //    unnormalised partial (acc, m, l) to the workspace; a merge kernel then
 //    combines the partitions by the log-sum-exp identity ([Int] "The kernel
@@ -69,7 +68,6 @@ constexpr int kMaxWaves = 8;        // decode workgroups have 4 or 8 waves (chos
 constexpr int kStepTokens = 16;     // tokens per wave step
 constexpr int kTableChunk = 1024;   // block-table entries staged in LDS at once
 constexpr int kRankMaxSeqs = 256;   // longest-first scheduling up to this batch
-constexpr int kRankMinCtx = 64;     // ... and only above this max_context_len
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -3.402823466e38f;  // running-max start (finite)
 
@@ -1470,11 +1468,8 @@ static hipError_t launch_typed(const DecodeLaunch &l, hipStream_t st) {
     a.hg = 1;
     a.ips = l.Hkv;
     // Ranking costs the workgroup one dependent round trip; it pays only when
-    // the grid is too large to be resident at once, so that order matters,
-    // and when a sequence can hold more than kRankMinCtx tokens: items of at
-    // most four 16-token steps differ by less than that round trip costs.
-    a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512 &&
-              l.max_ctx > kRankMinCtx) ? 1 : 0;
+    // the grid is too large to be resident at once, so that order matters.
+    a.rank = (l.PS == 0 && l.S > 1 && l.S <= kRankMaxSeqs && (int64_t)l.S * l.Hkv > 512) ? 1 : 0;
     {
         const int64_t span = l.PS ? (l.PS < l.max_ctx ? l.PS : l.max_ctx) : l.max_ctx;
         a.spec_blocks = (int32_t)((span + B - 1) / B);

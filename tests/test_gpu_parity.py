@@ -473,20 +473,29 @@ def test_binding_refuses_mismatched_head_dim():
 @pytest.mark.parametrize("dtype,hq,hkv", [("f16", 16, 16), ("bf16", 64, 16)])
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_order_does_not_change_bits(dtype, hq, hkv, layout):
-    """The same batch (every context at most 64 tokens, more than 512
-    workgroups) decoded without longest-first order (max_context_len 64)
-    and with it (max_context_len 65, the same clamped lengths): which
-    workgroup computes a row never changes its arithmetic, so the bits are
-    equal, and both match the oracle."""
+    """The same 64 sequences decoded with longest-first order (1024
+    workgroups) in their own order, reversed and in a random order: the
+    ranking hands each sequence to a different workgroup in each launch,
+    which never changes its arithmetic at one launch shape (the wave count,
+    which splits a sequence's steps among waves, is the same), so every row
+    has the same bits in all three, and they match the oracle."""
     rng = np.random.default_rng(4200 + hq)
     S = 64
-    lens = rng.integers(0, 65, size=S)
+    lens = rng.integers(0, 200, size=S)
     lens[::9] = 64
     lens[4::11] = 0
     lens[6::13] = 1
-    p = W.random_paged(4300 + hq, dtype, lens, hq, hkv, 128, extra_blocks=2, mbs=5)
-    t = upload(p, layout)
-    plain = run_decode(p, max_context_len=64, tensors=t, layout=layout)
-    ranked = run_decode(p, max_context_len=65, tensors=t, layout=layout)
-    assert same_bits(plain, ranked), f"{dtype} {layout}: order changed the bits"
-    check(p, ranked, ref_decode(p), f"order {dtype} {layout}")
+    p = W.random_paged(4300 + hq, dtype, lens, hq, hkv, 128, extra_blocks=2)
+
+    def sub(idx):
+        return W.Paged(dtype, np.ascontiguousarray(p.q[idx]), p.k_cache, p.v_cache,
+                       np.ascontiguousarray(p.block_tables[idx]),
+                       np.ascontiguousarray(p.context_lens[idx]), p.scale, p.block_size)
+
+    mcl = int(lens.max())
+    whole = run_decode(p, max_context_len=mcl, layout=layout)
+    for name, perm in (("reversed", np.arange(S)[::-1]), ("shuffled", rng.permutation(S))):
+        got = np.empty_like(whole)
+        got[perm] = run_decode(sub(perm), max_context_len=mcl, layout=layout)
+        assert same_bits(whole, got), f"{dtype} {layout}: batch {name}"
+    check(p, whole, ref_decode(p), f"order {dtype} {layout}")
